@@ -1,0 +1,139 @@
+"""MiniMax Sparse Attention (MSA) hot path for AMD MI355X: Python binding of libmsa.so.
+
+Each function has the name of the C entry point it calls (see include/msa.h) and only
+marshals arguments: torch tensors become device pointers, the current HIP stream is passed
+along, and a non-OK status raises MSAError.  All computation happens in the HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from ._lib import EXPORTS, MsaBatch, MsaCache, MSAError, check, load  # noqa: F401
+
+__all__ = ["Batch", "MSAError", "msa_index_score", "msa_topk_blocks", "msa_build_sparse_page_table",
+           "msa_sparse_attn_decode", "msa_sparse_attn_decode_workspace_size", "msa_sparse_attn_prefill",
+           "msa_sparse_attn_prefill_workspace_size", "msa_lse_merge", "msa_version", "load"]
+
+
+def _ptr(t: Optional[torch.Tensor], dtype, name: str, allow_none: bool = False) -> Optional[int]:
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _cache(t: torch.Tensor, name: str) -> MsaCache:
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [pages, block, heads, dim]")
+    P, BS, H, D = t.shape
+    return MsaCache(_ptr(t, torch.bfloat16, name), P, BS, H, D)
+
+
+class Batch:
+    """Requests and query rows (all int32 GPU tensors): block_table [B, max_blocks], ctx_len [B],
+    cu_q [B+1], q_pos [Nq].  ``max_q_per_request`` is the host-side bound on queries per request."""
+
+    def __init__(self, block_table, ctx_len, cu_q, q_pos, max_q_per_request: int):
+        self.block_table, self.ctx_len, self.cu_q, self.q_pos = block_table, ctx_len, cu_q, q_pos
+        self.max_q_per_request = int(max_q_per_request)
+        B = ctx_len.shape[0]
+        if block_table.dim() != 2 or block_table.shape[0] != B or cu_q.shape[0] != B + 1:
+            raise ValueError("block_table must be [B, max_blocks] and cu_q [B+1]")
+        self._c = MsaBatch(B, q_pos.shape[0], block_table.shape[1], self.max_q_per_request,
+                           _ptr(block_table, torch.int32, "block_table"), _ptr(ctx_len, torch.int32, "ctx_len"),
+                           _ptr(cu_q, torch.int32, "cu_q"), _ptr(q_pos, torch.int32, "q_pos"))
+
+    @property
+    def num_requests(self) -> int:
+        return self._c.num_requests
+
+    @property
+    def num_queries(self) -> int:
+        return self._c.num_queries
+
+    @property
+    def max_blocks(self) -> int:
+        return self._c.max_blocks
+
+    def ref(self):
+        return ctypes.byref(self._c)
+
+
+def msa_index_score(batch: Batch, q_idx, k_idx, scores, stream=None) -> None:
+    check("msa_index_score", load().msa_index_score(batch.ref(), _ptr(q_idx, torch.bfloat16, "q_idx"),
+                                                     _cache(k_idx, "k_idx"), _ptr(scores, torch.float32, "scores"),
+                                                     _stream(stream)))
+
+
+def msa_topk_blocks(batch: Batch, num_kv_heads: int, scores, k: int, sel, cnt, stream=None) -> None:
+    check("msa_topk_blocks", load().msa_topk_blocks(batch.ref(), num_kv_heads, _ptr(scores, torch.float32, "scores"),
+                                                     k, _ptr(sel, torch.int32, "sel"), _ptr(cnt, torch.int32, "cnt"),
+                                                     _stream(stream)))
+
+
+def msa_build_sparse_page_table(batch: Batch, num_kv_heads: int, num_pages: int, sel, cnt, k: int, page_table,
+                                row_len, stream=None) -> None:
+    check("msa_build_sparse_page_table",
+          load().msa_build_sparse_page_table(batch.ref(), num_kv_heads, num_pages, _ptr(sel, torch.int32, "sel"),
+                                             _ptr(cnt, torch.int32, "cnt"), k,
+                                             _ptr(page_table, torch.int32, "page_table"),
+                                             _ptr(row_len, torch.int32, "row_len"), _stream(stream)))
+
+
+def msa_sparse_attn_decode_workspace_size(rows: int, G: int, D: int, k: int) -> int:
+    return int(load().msa_sparse_attn_decode_workspace_size(rows, G, D, k))
+
+
+def msa_sparse_attn_decode(rows: int, G: int, D: int, q, k_base, v_base, page_stride: int, token_stride: int,
+                           page_table, k: int, row_len, sm_scale: float, out, lse, workspace, stream=None) -> None:
+    check("msa_sparse_attn_decode",
+          load().msa_sparse_attn_decode(rows, G, D, _ptr(q, torch.bfloat16, "q"), _ptr(k_base, torch.bfloat16, "k"),
+                                        _ptr(v_base, torch.bfloat16, "v"), page_stride, token_stride,
+                                        _ptr(page_table, torch.int32, "page_table"), k,
+                                        _ptr(row_len, torch.int32, "row_len"), sm_scale,
+                                        _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse", True),
+                                        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                        _stream(stream)))
+
+
+def msa_sparse_attn_prefill_workspace_size(num_queries: int, num_kv_heads: int, k: int, num_pages: int) -> int:
+    return int(load().msa_sparse_attn_prefill_workspace_size(num_queries, num_kv_heads, k, num_pages))
+
+
+def msa_sparse_attn_prefill(batch: Batch, G: int, q, k_cache, v_cache, sel, cnt, k: int, sm_scale: float, part_o,
+                            part_lse, workspace, stream=None) -> None:
+    check("msa_sparse_attn_prefill",
+          load().msa_sparse_attn_prefill(batch.ref(), G, _ptr(q, torch.bfloat16, "q"), _cache(k_cache, "k_cache"),
+                                         _cache(v_cache, "v_cache"), _ptr(sel, torch.int32, "sel"),
+                                         _ptr(cnt, torch.int32, "cnt"), k, sm_scale,
+                                         _ptr(part_o, torch.bfloat16, "part_o"),
+                                         _ptr(part_lse, torch.float32, "part_lse"),
+                                         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                         _stream(stream)))
+
+
+def msa_lse_merge(rows: int, parts: int, G: int, D: int, part_o, part_lse, out, lse_out, stream=None) -> None:
+    check("msa_lse_merge", load().msa_lse_merge(rows, parts, G, D, _ptr(part_o, torch.bfloat16, "part_o"),
+                                                 _ptr(part_lse, torch.float32, "part_lse"),
+                                                 _ptr(out, torch.bfloat16, "out"),
+                                                 _ptr(lse_out, torch.float32, "lse_out", True), _stream(stream)))
+
+
+def msa_version() -> int:
+    return int(load().msa_version())

@@ -1,0 +1,235 @@
+// Stage 1 of MSA: block index scores.
+//
+// score[t, g, b] = max over the valid tokens s of block b of q_idx[t, g] . k_idx[s, g]
+// (the max is this library's reading of "each 128-token block is reduced to one score",
+// Chinese page of the MiniMax-M3 serving write-up, section "索引评分器成为解码关键路径").
+//
+// Two kernels, picked by queries per request:
+//  * k_score_decode: one workgroup per (request, block).  The 128-token key-index block is
+//    the MFMA M dimension and the request's (at most 16) queries are padded only into N
+//    -- the AB-swapped layout the pages describe for the decode scorer.  Each page of the
+//    key-index cache is read exactly once per request, straight from HBM into MFMA
+//    operand registers (every 16-lane group reads whole 64-byte segments of a token row).
+//  * k_score_prefill: one workgroup per (256 query rows, KV head).  A GEMM over the causal
+//    range, staging each key-index block in LDS once for 256 queries whose index vectors
+//    stay in registers, with the per-block max fused into the epilogue so that token-level
+//    scores never reach memory.
+#include "msa_device.h"
+
+namespace msa {
+
+template <int DI>
+__global__ __launch_bounds__(256) void k_score_decode(
+    const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ ctx_len,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q_idx,
+    const bf16* __restrict__ kidx, int Hkv, float* __restrict__ scores) {
+  constexpr int KW = DI / 32;
+  __shared__ float red[4][64][16];
+  const int b = blockIdx.x, r = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, qd = lane >> 4;
+  const int q0 = cu_q[r], nq = cu_q[r + 1] - q0, L = ctx_len[r];
+
+  for (int qc = 0; qc < nq; qc += 16) {
+    const int nqc = min(16, nq - qc);
+    const int my_t = q0 + qc + n;
+    const int pos = (n < nqc) ? q_pos[my_t] : -1;
+    int maxpos = pos;
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) maxpos = max(maxpos, __shfl_xor(maxpos, m, kWave));
+
+    if (b * kBlock > maxpos) {  // not a candidate of any query in this chunk
+      for (int e = tid; e < nqc * Hkv; e += 256) {
+        const int t = q0 + qc + e / Hkv, g = e % Hkv;
+        scores[((int64_t)t * Hkv + g) * max_blocks + b] = neg_inf();
+      }
+      continue;
+    }
+    const int page = block_table[(int64_t)r * max_blocks + b];
+    const bf16* kb = kidx + (int64_t)page * kBlock * Hkv * DI;
+    const int tok_base = b * kBlock + 32 * w + 4 * qd;
+
+#pragma unroll 2
+    for (int g = 0; g < Hkv; ++g) {
+      u32x4 qf[KW];
+#pragma unroll
+      for (int kw = 0; kw < KW; ++kw)
+        qf[kw] = (n < nqc) ? ld16(q_idx + ((int64_t)my_t * Hkv + g) * DI + 32 * kw + 8 * qd) : zero4();
+      u32x4 a[2][KW];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int tok = 32 * w + 16 * sub + n;
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw)
+          a[sub][kw] = ld16(kb + ((int64_t)tok * Hkv + g) * DI + 32 * kw + 8 * qd);
+      }
+      float m = neg_inf();
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        f32x4 acc = fzero4();
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw) acc = mfma_bf16(a[sub][kw], qf[kw], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = tok_base + 16 * sub + i;
+          if (s <= pos && s < L) m = fmaxf(m, acc[i]);
+        }
+      }
+      m = max_over_quads(m);
+      if (qd == 0) red[w][g][n] = m;
+    }
+    __syncthreads();
+    for (int e = tid; e < nqc * Hkv; e += 256) {
+      const int qq = e / Hkv, g = e % Hkv;
+      const float v = fmaxf(fmaxf(red[0][g][qq], red[1][g][qq]), fmaxf(red[2][g][qq], red[3][g][qq]));
+      scores[((int64_t)(q0 + qc + qq) * Hkv + g) * max_blocks + b] = v;
+    }
+    __syncthreads();
+  }
+}
+
+constexpr int kPrefTQ = 256;  // query rows per workgroup (64 per wave)
+constexpr int kPrefSB = 16;   // blocks buffered per score flush
+
+template <int DI>
+__global__ __launch_bounds__(256) void k_score_prefill(
+    int B, int Nq, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ ctx_len,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q_idx,
+    const bf16* __restrict__ kidx, int Hkv, float* __restrict__ scores) {
+  constexpr int KW = DI / 32;
+  constexpr int KPAD = DI + 8;  // LDS row stride (elements): 16-lane ds_read_b128 groups hit 64 distinct banks
+  __shared__ __attribute__((aligned(16))) bf16 ks[kBlock * KPAD];
+  __shared__ float sbuf[kPrefTQ][kPrefSB + 1];
+  __shared__ int wred[2][4];
+
+  const int g = blockIdx.x % Hkv;  // consecutive workgroups take consecutive KV heads
+  const int row0 = (blockIdx.x / Hkv) * kPrefTQ;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, qd = lane >> 4;
+  const int last_row = min(row0 + kPrefTQ, Nq) - 1;
+  const int r_first = request_of(cu_q, B, row0), r_last = request_of(cu_q, B, last_row);
+
+  for (int r = r_first; r <= r_last; ++r) {
+    const int qa = max(row0, cu_q[r]), qb = min(row0 + kPrefTQ, cu_q[r + 1]);
+    if (qa >= qb) continue;  // uniform across the workgroup
+    const int L = ctx_len[r];
+
+    u32x4 qf[4][KW];
+    int pos[4];
+    int pmax = -1, pmin = 0x7fffffff;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int row = row0 + 64 * w + 16 * nt + n;
+      const bool in = row >= qa && row < qb;
+      pos[nt] = in ? q_pos[row] : -1;
+      if (in) { pmax = max(pmax, pos[nt]); pmin = min(pmin, pos[nt]); }
+#pragma unroll
+      for (int kw = 0; kw < KW; ++kw)
+        qf[nt][kw] = in ? ld16(q_idx + ((int64_t)row * Hkv + g) * DI + 32 * kw + 8 * qd) : zero4();
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      pmax = max(pmax, __shfl_xor(pmax, m, kWave));
+      pmin = min(pmin, __shfl_xor(pmin, m, kWave));
+    }
+    if (lane == 0) { wred[0][w] = pmax; wred[1][w] = pmin; }
+    __syncthreads();
+    pmax = max(max(wred[0][0], wred[0][1]), max(wred[0][2], wred[0][3]));
+    pmin = min(min(wred[1][0], wred[1][1]), min(wred[1][2], wred[1][3]));
+    const int nb = pmax / kBlock + 1;  // blocks needed by at least one row
+
+    for (int b0 = 0; b0 < nb; b0 += kPrefSB) {
+      const int b1 = min(b0 + kPrefSB, nb);
+      for (int b = b0; b < b1; ++b) {
+        const int page = block_table[(int64_t)r * max_blocks + b];
+        const bf16* kb = kidx + ((int64_t)page * kBlock * Hkv + g) * DI;
+        u32x4 stage[DI / 16];
+#pragma unroll
+        for (int c = 0; c < DI / 16; ++c) {
+          const int idx = tid + 256 * c, tok = idx / (DI / 8), ch = idx % (DI / 8);
+          stage[c] = ld16(kb + (int64_t)tok * Hkv * DI + ch * 8);
+        }
+        __syncthreads();  // previous block fully consumed
+#pragma unroll
+        for (int c = 0; c < DI / 16; ++c) {
+          const int idx = tid + 256 * c, tok = idx / (DI / 8), ch = idx % (DI / 8);
+          st16(&ks[tok * KPAD + ch * 8], stage[c]);
+        }
+        __syncthreads();
+
+        const bool full = (b * kBlock + kBlock - 1 <= pmin) && (b * kBlock + kBlock - 1 < L);
+        float mx[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
+#pragma unroll 2
+        for (int mt = 0; mt < 8; ++mt) {
+          u32x4 a[KW];
+#pragma unroll
+          for (int kw = 0; kw < KW; ++kw) a[kw] = ld16(&ks[(16 * mt + n) * KPAD + 32 * kw + 8 * qd]);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            f32x4 acc = fzero4();
+#pragma unroll
+            for (int kw = 0; kw < KW; ++kw) acc = mfma_bf16(a[kw], qf[nt][kw], acc);
+            if (full) {
+              mx[nt] = fmaxf(mx[nt], fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int s = b * kBlock + 16 * mt + 4 * qd + i;
+                if (s <= pos[nt] && s < L) mx[nt] = fmaxf(mx[nt], acc[i]);
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const float v = max_over_quads(mx[nt]);
+          if (qd == 0) sbuf[64 * w + 16 * nt + n][b - b0] = v;
+        }
+      }
+      __syncthreads();
+      // flush: 16 consecutive threads write 16 consecutive blocks of one row
+      for (int it = 0; it < kPrefTQ / 16; ++it) {
+        const int lrow = it * 16 + (tid >> 4), bb = tid & 15, row = row0 + lrow, b = b0 + bb;
+        if (row >= qa && row < qb && b < b1) scores[((int64_t)row * Hkv + g) * max_blocks + b] = sbuf[lrow][bb];
+      }
+    }
+    // non-candidate tail
+    const int tail = max_blocks - nb;
+    for (int e = tid; e < (qb - qa) * tail; e += 256) {
+      const int row = qa + e / tail, b = nb + e % tail;
+      scores[((int64_t)row * Hkv + g) * max_blocks + b] = neg_inf();
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_score_decode(int B, int Di, const int32_t* block_table, int max_blocks, const int32_t* ctx_len,
+                               const int32_t* cu_q, const int32_t* q_pos, const void* q_idx, const void* kidx,
+                               int Hkv, float* scores, hipStream_t stream) {
+  dim3 grid(max_blocks, B), block(256);
+  const bf16* qi = static_cast<const bf16*>(q_idx);
+  const bf16* ki = static_cast<const bf16*>(kidx);
+  if (Di == 128)
+    hipLaunchKernelGGL(k_score_decode<128>, grid, block, 0, stream, block_table, max_blocks, ctx_len, cu_q, q_pos,
+                       qi, ki, Hkv, scores);
+  else
+    hipLaunchKernelGGL(k_score_decode<64>, grid, block, 0, stream, block_table, max_blocks, ctx_len, cu_q, q_pos,
+                       qi, ki, Hkv, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_prefill(int B, int Nq, int Di, const int32_t* block_table, int max_blocks,
+                                const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const void* q_idx,
+                                const void* kidx, int Hkv, float* scores, hipStream_t stream) {
+  const int tiles = (Nq + kPrefTQ - 1) / kPrefTQ;
+  dim3 grid(tiles * Hkv), block(256);
+  const bf16* qi = static_cast<const bf16*>(q_idx);
+  const bf16* ki = static_cast<const bf16*>(kidx);
+  if (Di == 128)
+    hipLaunchKernelGGL(k_score_prefill<128>, grid, block, 0, stream, B, Nq, block_table, max_blocks, ctx_len, cu_q,
+                       q_pos, qi, ki, Hkv, scores);
+  else
+    hipLaunchKernelGGL(k_score_prefill<64>, grid, block, 0, stream, B, Nq, block_table, max_blocks, ctx_len, cu_q,
+                       q_pos, qi, ki, Hkv, scores);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,167 @@
+// Top-k over KV blocks per (query row, KV head), and the decode sparse page table.
+//
+// Top-k (Chinese page of the MiniMax-M3 serving write-up, sections "MiniMax稀疏注意力改变了服务问题"
+// and "遗留问题"): the k best candidate blocks by score; equal scores prefer the lower block
+// id; output in ascending block id with -1 padding.  One wavefront per row runs a radix
+// select on order-preserving 32-bit keys: it skips the bits every candidate shares, then
+// takes 8-bit digits from the top with an LDS histogram per pass, stopping as soon as the
+// boundary digit's bucket is taken whole.  A final in-order ballot pass writes the chosen
+// ids, which gives ascending order and the lower-id tie rule for free.
+#include "msa_device.h"
+
+namespace msa {
+
+__global__ __launch_bounds__(64) void k_topk(int B, int Hkv, int max_blocks, const int32_t* __restrict__ cu_q,
+                                             const int32_t* __restrict__ q_pos, const float* __restrict__ scores,
+                                             int k, int32_t* __restrict__ sel, int32_t* __restrict__ cnt) {
+  __shared__ uint32_t hist[256];
+  const int row = blockIdx.x;  // t*Hkv + g
+  const int t = row / Hkv;
+  const int lane = threadIdx.x;
+  const int n = min(q_pos[t] / kBlock + 1, max_blocks);
+  const float* s = scores + (int64_t)row * max_blocks;
+  int32_t* out = sel + (int64_t)row * k;
+
+  if (n <= k) {
+    for (int i = lane; i < k; i += kWave) out[i] = i < n ? i : -1;
+    if (lane == 0) cnt[row] = n;
+    return;
+  }
+
+  // bits shared by every candidate key need no pass
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int i = lane; i < n; i += kWave) {
+    const uint32_t key = order_key(s[i]);
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
+  }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, m, kWave));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m, kWave));
+  }
+  uint32_t prefix, mask;
+  int remaining = k;
+  if (kmin == kmax) {
+    prefix = kmin;
+    mask = 0xffffffffu;
+  } else {
+    const int hb = 31 - __builtin_clz(kmin ^ kmax);  // highest differing bit
+    mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
+    prefix = kmin & mask;
+    int top = hb;  // next digit covers bits [top-7, top] (clamped at bit 0)
+    while (top >= 0) {
+      const int lo = max(top - 7, 0);
+      const int width = top - lo + 1;
+      const uint32_t dmask = ((1u << width) - 1u);
+      for (int i = lane; i < 256; i += kWave) hist[i] = 0u;
+      __syncthreads();
+      for (int i = lane; i < n; i += kWave) {
+        const uint32_t key = order_key(s[i]);
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> lo) & dmask], 1u);
+      }
+      __syncthreads();
+      // lane l owns digits 255-4l .. 252-4l (descending); an inclusive scan over lanes gives
+      // the number of keys whose digit is at least a given value
+      uint32_t c[4], local = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; local += c[j]; }
+      uint32_t incl = local;
+#pragma unroll
+      for (int m = 1; m < kWave; m <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_up((int)incl, m, kWave);
+        if (lane >= m) incl += o;
+      }
+      uint32_t before = incl - local;
+      int found = -1;
+      uint32_t found_before = 0, found_cnt = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (found < 0 && before < (uint32_t)remaining && before + c[j] >= (uint32_t)remaining) {
+          found = 255 - 4 * lane - j;
+          found_before = before;
+          found_cnt = c[j];
+        }
+        before += c[j];
+      }
+      const uint64_t hit = __ballot(found >= 0);
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      const int digit = __shfl(found, src, kWave);
+      const uint32_t gt = (uint32_t)__shfl((int)found_before, src, kWave);
+      const uint32_t eq = (uint32_t)__shfl((int)found_cnt, src, kWave);
+      remaining -= (int)gt;
+      prefix |= ((uint32_t)digit) << lo;
+      mask |= dmask << lo;
+      __syncthreads();
+      if (eq == (uint32_t)remaining) break;  // the whole boundary bucket is taken
+      top = lo - 1;
+    }
+  }
+
+  // emit in id order: keys above the boundary, then the first `remaining` boundary ties
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int written = 0, ties_seen = 0;
+  for (int base = 0; base < n; base += kWave) {
+    const int i = base + lane;
+    const uint32_t hk = (i < n) ? (order_key(s[i]) & mask) : 0u;
+    const bool gt = i < n && hk > prefix;
+    const bool eq = i < n && hk == prefix;
+    const uint64_t eqm = __ballot(eq);
+    const int eq_rank = ties_seen + __popcll(eqm & lt_mask);
+    const bool take = gt || (eq && eq_rank < remaining);
+    const uint64_t tm = __ballot(take);
+    const int slot = written + __popcll(tm & lt_mask);
+    if (take && slot < k) out[slot] = i;
+    written += __popcll(tm);
+    ties_seen += __popcll(eqm);
+  }
+  written = min(written, k);
+  for (int i = written + lane; i < k; i += kWave) out[i] = -1;
+  if (lane == 0) cnt[row] = written;
+}
+
+// Decode sparse page table over the strided view (Chinese page, section "MSA需要新的分页注意力集成"):
+// row rho = t*Hkv + g, page_table[rho, j] = block_table[r, sel[t,g,j]] * 128 * Hkv + g.
+__global__ __launch_bounds__(256) void k_page_table(int rows, int B, int Hkv, int max_blocks,
+                                                    const int32_t* __restrict__ block_table,
+                                                    const int32_t* __restrict__ ctx_len,
+                                                    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ q_pos,
+                                                    const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
+                                                    int k, int32_t* __restrict__ page_table,
+                                                    int32_t* __restrict__ row_len) {
+  const int rho = blockIdx.x * blockDim.x + threadIdx.x;
+  if (rho >= rows) return;
+  const int t = rho / Hkv, g = rho % Hkv;
+  const int r = request_of(cu_q, B, t);
+  const int lim = min(q_pos[t] + 1, ctx_len[r]);  // tokens s < lim are valid
+  const int c = cnt[rho];
+  int len = 0;
+  for (int j = 0; j < k; ++j) {
+    int v = -1;
+    if (j < c) {
+      const int bl = sel[(int64_t)rho * k + j];
+      v = block_table[(int64_t)r * max_blocks + bl] * (kBlock * Hkv) + g;
+      len += min(kBlock, lim - bl * kBlock);
+    }
+    page_table[(int64_t)rho * k + j] = v;
+  }
+  row_len[rho] = len;
+}
+
+hipError_t launch_topk(int B, int Nq, int Hkv, int max_blocks, const int32_t* cu_q, const int32_t* q_pos,
+                       const float* scores, int k, int32_t* sel, int32_t* cnt, hipStream_t stream) {
+  hipLaunchKernelGGL(k_topk, dim3(Nq * Hkv), dim3(64), 0, stream, B, Hkv, max_blocks, cu_q, q_pos, scores, k, sel,
+                     cnt);
+  return hipGetLastError();
+}
+
+hipError_t launch_page_table(int B, int Nq, int Hkv, int max_blocks, const int32_t* block_table,
+                             const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const int32_t* sel,
+                             const int32_t* cnt, int k, int32_t* page_table, int32_t* row_len, hipStream_t stream) {
+  const int rows = Nq * Hkv;
+  hipLaunchKernelGGL(k_page_table, dim3((rows + 255) / 256), dim3(256), 0, stream, rows, B, Hkv, max_blocks,
+                     block_table, ctx_len, cu_q, q_pos, sel, cnt, k, page_table, row_len);
+  return hipGetLastError();
+}
+
+}  // namespace msa

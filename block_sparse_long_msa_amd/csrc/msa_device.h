@@ -1,0 +1,79 @@
+// Device-side helpers shared by the MSA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kBlock = 128;      // tokens per KV block (= page)
+constexpr int kWave = 64;
+
+typedef uint16_t bf16;           // storage type: raw bfloat16 bits
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+__device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// float -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ u32x4 zero4() { u32x4 z = {0u, 0u, 0u, 0u}; return z; }
+__device__ __forceinline__ f32x4 fzero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+// D(16x16, f32) += A(16x32, bf16) * B(32x16, bf16).
+// Lane l supplies A[l%16][k in chunk l/16] and B[k in chunk l/16][l%16] (8 values each, the
+// same k order on both sides); it receives D[4*(l/16)+i][l%16], i = 0..3.
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+// D(16x16, f32) += A(16x4, f32) * B(4x16, f32): lane l supplies A[l%16][l/16], B[l/16][l%16].
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+// Reduce across the four 16-lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max_over_quads(float v) {
+  v = fmaxf(v, shfl_xor(v, 16));
+  return fmaxf(v, shfl_xor(v, 32));
+}
+__device__ __forceinline__ float sum_over_quads(float v) {
+  v += shfl_xor(v, 16);
+  return v + shfl_xor(v, 32);
+}
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// Order-preserving map of a float to uint32 (-0 is folded onto +0 so equal scores tie).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f == 0.0f) f = 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Request that owns query row t (cu_q is non-decreasing, cu_q[0] = 0, cu_q[B] = Nq).
+__device__ __forceinline__ int request_of(const int32_t* __restrict__ cu_q, int B, int t) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace msa

@@ -1,0 +1,85 @@
+"""One MSA layer invocation as a chain of C-ABI calls with preallocated buffers.
+
+MSADecode: index scores -> top-k -> sparse page table -> decode attention (split over pages,
+           merged in the library).
+MSAPrefill: index scores -> top-k -> KV-block-major attention (partials) -> LSE merge.
+
+Buffers are allocated once with torch (device memory only); every step runs in libmsa.so.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (Batch, msa_build_sparse_page_table, msa_index_score, msa_lse_merge, msa_sparse_attn_decode,
+               msa_sparse_attn_decode_workspace_size, msa_sparse_attn_prefill,
+               msa_sparse_attn_prefill_workspace_size, msa_topk_blocks)
+
+
+class MSADecode:
+    def __init__(self, batch: Batch, Hkv: int, G: int, D: int, k: int, num_pages: int, device="cuda"):
+        Nq, mb = batch.num_queries, batch.max_blocks
+        self.batch, self.Hkv, self.G, self.D, self.k, self.num_pages = batch, Hkv, G, D, k, num_pages
+        self.rows = Nq * Hkv
+        self.scores = torch.empty((Nq, Hkv, mb), dtype=torch.float32, device=device)
+        self.sel = torch.empty((Nq, Hkv, k), dtype=torch.int32, device=device)
+        self.cnt = torch.empty((Nq, Hkv), dtype=torch.int32, device=device)
+        self.page_table = torch.empty((self.rows, k), dtype=torch.int32, device=device)
+        self.row_len = torch.empty((self.rows,), dtype=torch.int32, device=device)
+        self.out = torch.empty((Nq, Hkv * G, D), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((Nq, Hkv * G), dtype=torch.float32, device=device)
+        self.ws = torch.empty((msa_sparse_attn_decode_workspace_size(self.rows, G, D, k),), dtype=torch.uint8,
+                              device=device)
+
+    def score(self, q_idx, kidx, stream=None):
+        msa_index_score(self.batch, q_idx, kidx, self.scores, stream)
+
+    def select(self, stream=None):
+        msa_topk_blocks(self.batch, self.Hkv, self.scores, self.k, self.sel, self.cnt, stream)
+        msa_build_sparse_page_table(self.batch, self.Hkv, self.num_pages, self.sel, self.cnt, self.k,
+                                    self.page_table, self.row_len, stream)
+
+    def attend(self, q, kcache, vcache, sm_scale: float, stream=None):
+        msa_sparse_attn_decode(self.rows, self.G, self.D, q, kcache, vcache, self.D, self.Hkv * self.D,
+                               self.page_table, self.k, self.row_len, sm_scale, self.out, self.lse, self.ws, stream)
+
+    def __call__(self, q, q_idx, kcache, vcache, kidx, sm_scale: float, stream=None):
+        self.score(q_idx, kidx, stream)
+        self.select(stream)
+        self.attend(q, kcache, vcache, sm_scale, stream)
+        return self.out, self.lse
+
+
+class MSAPrefill:
+    def __init__(self, batch: Batch, Hkv: int, G: int, D: int, k: int, num_pages: int, device="cuda"):
+        Nq, mb = batch.num_queries, batch.max_blocks
+        self.batch, self.Hkv, self.G, self.D, self.k, self.num_pages = batch, Hkv, G, D, k, num_pages
+        self.scores = torch.empty((Nq, Hkv, mb), dtype=torch.float32, device=device)
+        self.sel = torch.empty((Nq, Hkv, k), dtype=torch.int32, device=device)
+        self.cnt = torch.empty((Nq, Hkv), dtype=torch.int32, device=device)
+        self.part_o = torch.empty((Nq, Hkv, k, G, D), dtype=torch.bfloat16, device=device)
+        self.part_lse = torch.empty((Nq, Hkv, k, G), dtype=torch.float32, device=device)
+        self.out = torch.empty((Nq, Hkv * G, D), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((Nq, Hkv * G), dtype=torch.float32, device=device)
+        self.ws = torch.empty((msa_sparse_attn_prefill_workspace_size(Nq, Hkv, k, num_pages),), dtype=torch.uint8,
+                              device=device)
+
+    def score(self, q_idx, kidx, stream=None):
+        msa_index_score(self.batch, q_idx, kidx, self.scores, stream)
+
+    def select(self, stream=None):
+        msa_topk_blocks(self.batch, self.Hkv, self.scores, self.k, self.sel, self.cnt, stream)
+
+    def attend(self, q, kcache, vcache, sm_scale: float, stream=None):
+        msa_sparse_attn_prefill(self.batch, self.G, q, kcache, vcache, self.sel, self.cnt, self.k, sm_scale,
+                                self.part_o, self.part_lse, self.ws, stream)
+
+    def merge(self, stream=None):
+        rows = self.batch.num_queries * self.Hkv
+        msa_lse_merge(rows, self.k, self.G, self.D, self.part_o, self.part_lse, self.out, self.lse, stream)
+
+    def __call__(self, q, q_idx, kcache, vcache, kidx, sm_scale: float, stream=None):
+        self.score(q_idx, kidx, stream)
+        self.select(stream)
+        self.attend(q, kcache, vcache, sm_scale, stream)
+        self.merge(stream)
+        return self.out, self.lse

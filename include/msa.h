@@ -1,0 +1,173 @@
+/*
+ * msa.h -- C ABI of the MiniMax Sparse Attention (MSA) hot path for AMD MI355X (gfx950).
+ *
+ * MSA has two stages: index scoring with a per-(request, KV group) top-k over 128-token
+ * KV blocks, then dense attention from each query to the selected blocks only
+ * (Together AI's MiniMax-M3 serving write-up, Chinese rendering, section
+ * "MiniMax稀疏注意力改变了服务问题"; Japanese rendering, "アーキテクチャ / 特徴").
+ * Prefill runs the attention KV-block-major, {kv block, q}, and combines the
+ * per-block partial outputs with a log-sum-exp reduction (section
+ * "KV块主序稀疏注意力减少冗余KV移动").  Decode folds the KV-group dimension into the
+ * batch and gives every flattened row its own page table over a strided view of
+ * the shared paged KV tensor (section "MSA需要新的分页注意力集成").
+ *
+ * Conventions for every call
+ *  - Memory: every array argument is DEVICE memory owned by the caller (typically a
+ *    PyTorch tensor's data pointer), except the msa_batch / msa_cache structs themselves,
+ *    which live in host memory and are read during the call only.  The library never
+ *    allocates, frees or synchronizes.  Arrays must be contiguous, 16-byte aligned.
+ *  - Types: bf16 arrays hold IEEE bfloat16 bit patterns; scores, log-sum-exps and
+ *    workspaces are float32; indices are int32.
+ *  - Streams: work is enqueued on `stream` (NULL = the legacy default stream) and is
+ *    asynchronous; results are ready when the stream reaches that point.
+ *  - Errors: arguments are validated on the host before anything is launched; an invalid
+ *    or unsupported argument returns MSA_ERR_INVALID_ARG / MSA_ERR_UNSUPPORTED and launches
+ *    nothing.  A failed launch returns MSA_ERR_HIP.  msa_last_error() gives a message for
+ *    the calling thread's last failure.  Device-side values are trusted: a block table
+ *    entry, position or selection outside the documented range is undefined behaviour.
+ *  - Determinism: results are bitwise reproducible for identical inputs (no float atomics).
+ *  - Thread safety: stateless; calls on different streams may run concurrently.
+ *  - Supported shapes: block_size = 128; D, Di in {64, 128}; G = Hq/Hkv in {1,2,4,8,16};
+ *    1 <= k <= 64; 1 <= Hkv <= 64.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t* msa_stream_t;
+
+typedef enum msa_status {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = 1,
+  MSA_ERR_UNSUPPORTED = 2,
+  MSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  MSA_ERR_HIP = 4
+} msa_status;
+
+/* A batch of requests and their query rows.  Request r owns the query rows
+ * cu_q[r] .. cu_q[r+1]-1; query row t sits at absolute position q_pos[t] < ctx_len[r]
+ * of its request, and its own key/value/index rows are already in the caches. */
+typedef struct msa_batch {
+  int32_t num_requests;        /* B >= 1 */
+  int32_t num_queries;         /* Nq >= 0, equals cu_q[B] */
+  int32_t max_blocks;          /* columns of block_table, >= ceil(ctx_len[r] / 128) for all r */
+  int32_t max_q_per_request;   /* host-side bound on cu_q[r+1]-cu_q[r]; picks the scorer shape */
+  const int32_t* block_table;  /* device [B, max_blocks]: physical page of logical block b */
+  const int32_t* ctx_len;      /* device [B]: L_r, tokens in the cache (current tokens included) */
+  const int32_t* cu_q;         /* device [B+1]: query row offsets, cu_q[0] = 0, non-decreasing */
+  const int32_t* q_pos;        /* device [Nq]: absolute position of each query row */
+} msa_batch;
+
+/* A paged cache: device bf16 [num_pages, block_size, num_heads, head_dim], contiguous. */
+typedef struct msa_cache {
+  const void* data;
+  int32_t num_pages;
+  int32_t block_size;          /* 128 */
+  int32_t num_heads;           /* Hkv */
+  int32_t head_dim;            /* D (keys/values) or Di (key index) */
+} msa_cache;
+
+/* Stage 1, index scoring (Chinese page, section "索引评分器成为解码关键路径"; Japanese page,
+ * "Decode Index Scoring Kernel Optimization"): the query-side index vector of every query
+ * row and KV head is dotted with the key-side index vector of every candidate token, and
+ * every 128-token block is reduced to one score, the MAX over its valid tokens (the pages
+ * leave the reduction open; max is this library's reading).
+ *   q_idx   device bf16 [Nq, Hkv, Di]
+ *   k_idx   key-index cache [pages, 128, Hkv, Di]
+ *   scores  device f32 [Nq, Hkv, max_blocks], fully written: scores[t,g,b] for the candidate
+ *           blocks b = 0 .. q_pos[t]/128, -inf for every other column.  A token s of a
+ *           candidate block counts iff s <= q_pos[t] and s < ctx_len[r].
+ * Rows of requests with at most 16 queries (batch->max_q_per_request <= 16) go to the
+ * decode kernel (one pass over each page per request, queries in the MFMA N dimension);
+ * larger query counts go to the prefill GEMM kernel. */
+msa_status msa_index_score(const msa_batch* batch, const void* q_idx, msa_cache k_idx, float* scores,
+                           msa_stream_t stream);
+
+/* Top-k over KV blocks (Chinese page, sections "MiniMax稀疏注意力改变了服务问题" and "遗留问题"):
+ * for each (query row t, KV head g) the min(k, n_cand) candidates with the highest scores,
+ * n_cand = q_pos[t]/128 + 1; equal scores prefer the lower block id.
+ *   scores  device f32 [Nq, Hkv, max_blocks] as written by msa_index_score
+ *   sel     device i32 [Nq, Hkv, k]: selected block ids in ascending order, -1 padding
+ *   cnt     device i32 [Nq, Hkv]: number of selected blocks */
+msa_status msa_topk_blocks(const msa_batch* batch, int32_t num_kv_heads, const float* scores, int32_t k,
+                           int32_t* sel, int32_t* cnt, msa_stream_t stream);
+
+/* Sparse per-row page table for decode (Chinese page, section "MSA需要新的分页注意力集成"):
+ * row rho = t*Hkv + g of the flattened (query row, KV head) batch gets
+ *   page_table[rho, j] = block_table[r, sel[t,g,j]] * 128 * Hkv + g   (j < cnt[t,g]; -1 after)
+ * a virtual page id in the strided view of a [pages, 128, Hkv, D] cache whose page
+ * stride is D elements and token stride Hkv*D elements, and
+ *   row_len[rho] = number of valid tokens over the selected blocks (only the last,
+ *                  highest block can be partial).
+ * num_pages is the page count of the cache; num_pages*128*Hkv must fit in int32.
+ *   page_table  device i32 [Nq*Hkv, k];  row_len  device i32 [Nq*Hkv] */
+msa_status msa_build_sparse_page_table(const msa_batch* batch, int32_t num_kv_heads, int32_t num_pages,
+                                       const int32_t* sel, const int32_t* cnt, int32_t k,
+                                       int32_t* page_table, int32_t* row_len, msa_stream_t stream);
+
+/* Decode attention over the sparse page table (same section): each row rho attends with its
+ * G query heads q[rho*G .. rho*G+G-1] to the first row_len[rho] tokens of its virtual pages.
+ * Token i of row rho is virtual page v = page_table[rho, i/128], slot s = i%128, and its
+ * element d is at k_base[v*page_stride + s*token_stride + d] (same for v_base).
+ * Softmax scale sm_scale, natural-log LSE.  Work is split over the row's pages and combined
+ * by a log-sum-exp merge through the workspace.
+ *   q        device bf16 [rows*G, D]  (= [Nq, Hq, D] when rows = Nq*Hkv)
+ *   out      device bf16 [rows*G, D]
+ *   lse      device f32 [rows*G] or NULL
+ *   workspace  device, >= msa_sparse_attn_decode_workspace_size(rows, G, D, k) bytes
+ * Rows with row_len = 0 are invalid input. */
+msa_status msa_sparse_attn_decode(int32_t rows, int32_t G, int32_t D, const void* q, const void* k_base,
+                                  const void* v_base, int64_t page_stride, int64_t token_stride,
+                                  const int32_t* page_table, int32_t k, const int32_t* row_len,
+                                  float sm_scale, void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, msa_stream_t stream);
+size_t msa_sparse_attn_decode_workspace_size(int32_t rows, int32_t G, int32_t D, int32_t k);
+
+/* KV-block-major prefill attention (section "KV块主序稀疏注意力减少冗余KV移动"; Russian page,
+ * third paragraph): the selection is inverted into {(KV head, physical page) -> queries}
+ * lists, each selected KV block is staged on chip and attended by every query row that
+ * picked it, and each (query row t, KV head g, slot j) gets the partial output of block
+ * sel[t,g,j] alone:
+ *   part_o[t,g,j,i,:] = softmax_i(scale * q[t, g*G+i] . K_b) V_b   (normalized, bf16)
+ *   part_lse[t,g,j,i] = log sum exp of the same logits            (f32; -inf for j >= cnt)
+ * Causal masking inside the block: key s counts iff s <= q_pos[t] and s < ctx_len[r].
+ *   q       device bf16 [Nq, Hkv*G, D]
+ *   k_cache, v_cache  [pages, 128, Hkv, D]
+ *   sel, cnt  from msa_topk_blocks
+ *   part_o  device bf16 [Nq, Hkv, k, G, D];  part_lse  device f32 [Nq, Hkv, k, G]
+ *   workspace  device, >= msa_sparse_attn_prefill_workspace_size(...) bytes
+ * Combine the partials with msa_lse_merge(rows = Nq*Hkv, parts = k, ...). */
+msa_status msa_sparse_attn_prefill(const msa_batch* batch, int32_t G, const void* q, msa_cache k_cache,
+                                   msa_cache v_cache, const int32_t* sel, const int32_t* cnt, int32_t k,
+                                   float sm_scale, void* part_o, float* part_lse, void* workspace,
+                                   size_t workspace_bytes, msa_stream_t stream);
+size_t msa_sparse_attn_prefill_workspace_size(int32_t num_queries, int32_t num_kv_heads, int32_t k,
+                                              int32_t num_pages);
+
+/* Log-sum-exp reduction of per-block partials (section "KV块主序稀疏注意力减少冗余KV移动"):
+ *   LSE = log sum_j exp(lse_j),  O = sum_j exp(lse_j - LSE) * O_j, over the parts with
+ *   lse_j > -inf (at least one per row and head).
+ *   part_o    device bf16 [rows, parts, G, D];  part_lse  device f32 [rows, parts, G]
+ *   out       device bf16 [rows, G, D];         lse_out   device f32 [rows, G] or NULL */
+msa_status msa_lse_merge(int64_t rows, int32_t parts, int32_t G, int32_t D, const void* part_o,
+                         const float* part_lse, void* out, float* lse_out, msa_stream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* msa_status_string(msa_status status);
+/* Message describing the calling thread's most recent failure ("" if none). */
+const char* msa_last_error(void);
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

@@ -76,6 +76,11 @@ def request_tokens(cache, block_table_row, ntok: int, block: int) -> np.ndarray:
 
 # --- stage 1: index scores ---------------------------------------------------
 
+def block_score(q_vec, k_rows, n_valid: int) -> float:
+    """R1: the score of one block is the max over its first n_valid token rows of q_vec . k_row."""
+    return float((_f64(k_rows)[:n_valid] @ _f64(q_vec)).max())
+
+
 def index_scores(q_idx, kidx_cache, block_table, ctx_len, q_req, q_pos, block, max_blocks=None):
     """Block scores [Nq, Hkv, max_blocks] (float64): score[t, g, b] is the max over valid
     tokens s of block b of q_idx[t, g] . k_idx[s, g]; non-candidate blocks hold -inf."""
@@ -84,17 +89,14 @@ def index_scores(q_idx, kidx_cache, block_table, ctx_len, q_req, q_pos, block, m
     if max_blocks is None:
         max_blocks = block_table.shape[1]
     out = np.full((Nq, Hkv, max_blocks), NEG_INF)
-    for r in np.unique(q_req):
-        rows = np.nonzero(q_req == r)[0]
+    for t in range(Nq):
+        r, p = int(q_req[t]), int(q_pos[t])
         L = int(ctx_len[r])
-        keys = request_tokens(kidx_cache, block_table[r], L, block)        # [L, Hkv, Di]
-        for g in range(Hkv):
-            dots = q_idx[rows, g, :] @ keys[:, g, :].T                    # [nrows, L]
-            for i, t in enumerate(rows):
-                p = int(q_pos[t])
-                for b in range(num_candidates(p, block)):
-                    n = valid_token_count(b, p, L, block)
-                    out[t, g, b] = dots[i, b * block: b * block + n].max()
+        for b in range(num_candidates(p, block)):
+            page = int(block_table[r, b])
+            n = valid_token_count(b, p, L, block)
+            for g in range(Hkv):
+                out[t, g, b] = block_score(q_idx[t, g], kidx_cache[page, :, g, :], n)
     return out
 
 
@@ -120,8 +122,9 @@ def topk_blocks(scores, q_pos, block, k):
 
 # --- stage 2: attention over the selected blocks ----------------------------
 
-def _softmax_attend(qv, keys, vals, scale):
-    """One query head over a key set: returns (o [D], lse)."""
+def attend(qv, keys, vals, scale):
+    """One query head over a key set: softmax(scale * keys . qv) applied to vals -> (o [D], lse)."""
+    qv, keys, vals = _f64(qv), _f64(keys), _f64(vals)
     logits = (keys @ qv) * scale
     m = logits.max()
     w = np.exp(logits - m)
@@ -138,6 +141,18 @@ def selected_token_ids(sel_row, cnt, pos, L, block):
     return np.asarray(ids, dtype=np.int64)
 
 
+def selected_kv(kcache, vcache, block_table_row, sel_row, cnt, g, pos, L, block):
+    """Keys and values [n, D] of the valid tokens of the selected blocks of KV head g, in
+    selection order (gathered page by page through the block table)."""
+    ks, vs = [], []
+    for b in sel_row[:cnt]:
+        n = valid_token_count(int(b), pos, L, block)
+        page = int(block_table_row[int(b)])
+        ks.append(_f64(kcache[page, :n, g]))
+        vs.append(_f64(vcache[page, :n, g]))
+    return np.concatenate(ks), np.concatenate(vs)
+
+
 def sparse_attention(q, kcache, vcache, block_table, ctx_len, q_req, q_pos, sel, cnt, block, scale):
     """out[t, h] = softmax(scale * q[t,h] . K_S) V_S over the union S of valid tokens of the blocks
     selected for (t, g = h // G); lse[t, h] = log sum exp of the same logits."""
@@ -147,18 +162,13 @@ def sparse_attention(q, kcache, vcache, block_table, ctx_len, q_req, q_pos, sel,
     G = Hq // Hkv
     out = np.zeros((Nq, Hq, D))
     lse = np.zeros((Nq, Hq))
-    cache_k, cache_v = {}, {}
     for t in range(Nq):
         r, p = int(q_req[t]), int(q_pos[t])
         L = int(ctx_len[r])
-        if r not in cache_k:
-            cache_k = {r: request_tokens(kcache, block_table[r], L, block)}
-            cache_v = {r: request_tokens(vcache, block_table[r], L, block)}
-        K, V = cache_k[r], cache_v[r]
         for g in range(Hkv):
-            ids = selected_token_ids(sel[t, g], int(cnt[t, g]), p, L, block)
+            K, V = selected_kv(kcache, vcache, block_table[r], sel[t, g], int(cnt[t, g]), g, p, L, block)
             for h in range(g * G, (g + 1) * G):
-                out[t, h], lse[t, h] = _softmax_attend(q[t, h], K[ids, g], V[ids, g], scale)
+                out[t, h], lse[t, h] = attend(q[t, h], K, V, scale)
     return out, lse
 
 
@@ -183,7 +193,7 @@ def block_partials(q, kcache, vcache, block_table, ctx_len, q_req, q_pos, sel, c
                 K = _f64(kcache[page, :n, g])
                 V = _f64(vcache[page, :n, g])
                 for i in range(G):
-                    po[t, g, j, i], pl[t, g, j, i] = _softmax_attend(q[t, g * G + i], K, V, scale)
+                    po[t, g, j, i], pl[t, g, j, i] = attend(q[t, g * G + i], K, V, scale)
     return po, pl
 
 
@@ -242,7 +252,7 @@ def paged_decode_attention(q, k_flat, v_flat, page_table, row_len, page_stride, 
         addr = v[:, None] * page_stride + (i % block)[:, None] * token_stride + d[None, :]
         K, V = kf[addr], vf[addr]
         for h in range(G):
-            out[rho, h], lse[rho, h] = _softmax_attend(q[rho, h], K, V, scale)
+            out[rho, h], lse[rho, h] = attend(q[rho, h], K, V, scale)
     return out, lse
 
 
