@@ -1,0 +1,267 @@
+"""Benchmark one MSA layer invocation on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload agentic_decode|long_prefill|...]
+
+A step is one pass of the whole MSA hot path over one synthetic batch with every input already
+resident in HBM: decode = index scores -> top-k -> sparse page table -> decode attention (+merge);
+prefill = index scores -> top-k -> KV-block-major attention -> LSE merge.  Each timed step is
+bracketed by HIP events on the stream the kernels run on; a 1 GiB buffer is READ before every
+step (outside the events) so that no step finds the previous step's pages in L2 or the MALL (a
+write-based flush would leave dirty lines whose write-back competes with the timed kernels).
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import msa_inputs as mi  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "MSA prefill/decode tokens/s; scorer HBM GB/s and attn MFMA % of peak, 1 GPU"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="agentic_decode", choices=sorted(mi.WORKLOADS))
+    p.add_argument("--batch", type=int, default=None, help="batch for million_decode (1 or 4)")
+    p.add_argument("--no-flush", action="store_true", help="do not read 1 GiB between steps")
+    p.add_argument("--cpu-budget-s", type=float, default=12.0, help="oracle time budget for cpu_baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after timing, run one plain 1 GiB device copy (reference for HBM byte counters)")
+    return p.parse_args()
+
+
+def make_workload(name, batch):
+    if name == "million_decode":
+        return mi.million_decode(batch=batch or 1)
+    return mi.WORKLOADS[name]()
+
+
+# --- algorithmic work per launch ----------------------------------------------------------
+
+def candidate_tokens(wl):
+    """Sum over (query row) of its candidate tokens: tokens 0 .. pos (all valid, pos < L)."""
+    total = 0
+    for L, nq in zip(wl.ctx_lens, wl.q_counts):
+        first = L - nq
+        total += sum(p + 1 for p in range(first, L))
+    return total
+
+
+def selected_tokens(dev, sel, cnt):
+    """Valid tokens over the selected blocks, summed over (query row, KV head)."""
+    BS = dev.wl.block
+    req = dev.q_req.long()
+    lim = torch.minimum(dev.q_pos.long() + 1, dev.ctx_len.long()[req])          # [Nq]
+    s = sel.long()
+    valid = torch.clamp(lim[:, None, None] - s * BS, min=0, max=BS)
+    mask = torch.arange(sel.shape[2], device=sel.device)[None, None, :] < cnt[:, :, None]
+    return int((valid * mask).sum().item())
+
+
+# --- cpu_baseline: the CPU oracle, timed on a bounded sample of the same workload ---------------
+
+def cpu_baseline(dev, budget_s: float):
+    """Time the CPU oracle (as it stands) on whole query rows of this workload until about
+    ``budget_s`` seconds of oracle time are spent.  Per sampled request the oracle sees only that
+    request's pages, copied to host memory outside the timed sections; BLAS is held to one thread
+    (the oracle's Python loops use one core)."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    wl = dev.wl
+    BS, Hkv, G, D = wl.block, wl.Hkv, wl.G, wl.D
+    host = lambda t: (t.float() if t.is_floating_point() else t).cpu().numpy()
+    bt, cu, pos_all = host(dev.block_table), host(dev.cu_q), host(dev.q_pos)
+    decode = max(wl.q_counts) <= 16
+    spent, tokens, sampled = 0.0, 0, []
+    with threadpool_limits(limits=1):
+        for r in range(wl.B):
+            L = wl.ctx_lens[r]
+            nb = -(-L // BS)
+            pages = torch.from_numpy(bt[r, :nb].astype(np.int64)).cuda()
+            kidx_r = host(dev.kidx[pages])                                  # [nb, BS, Hkv, Di]
+            local_bt = np.arange(nb, dtype=np.int64)[None]
+            lo, hi = int(cu[r]), int(cu[r + 1])
+            rows = np.arange(lo, hi) if decode else np.linspace(lo, hi - 1, num=min(hi - lo, 4096)).astype(int)
+            for c0 in range(0, len(rows), 8):
+                rr = rows[c0:c0 + 8]
+                qi, q, pos = host(dev.q_idx[rr]), host(dev.q[rr]), pos_all[rr]
+                req = np.zeros(len(rr), dtype=np.int64)
+                t0 = time.perf_counter()
+                sc = oracle.index_scores(qi, kidx_r, local_bt, np.asarray([L]), req, pos, BS)
+                sel, cnt = oracle.topk_blocks(sc, pos, BS, wl.k)
+                t1 = time.perf_counter()
+                need = np.unique(sel[sel >= 0])                              # selected blocks' pages only
+                compact = np.zeros((1, nb), dtype=np.int64)
+                compact[0, need] = np.arange(len(need))
+                pg = torch.from_numpy(bt[r, need].astype(np.int64)).cuda()
+                kc, vc = host(dev.kcache[pg]), host(dev.vcache[pg])
+                t2 = time.perf_counter()
+                if decode:
+                    pt, rl = oracle.sparse_page_table(sel, cnt, compact, np.asarray([L]), req, pos, Hkv, BS)
+                    oracle.paged_decode_attention(q.reshape(len(rr) * Hkv, G, D), kc, vc, pt, rl, D, Hkv * D, BS,
+                                                  dev.scale)
+                else:
+                    po, pl = oracle.block_partials(q, kc, vc, compact, np.asarray([L]), req, pos, sel, cnt, BS,
+                                                   dev.scale)
+                    oracle.lse_merge(po, pl)
+                t3 = time.perf_counter()
+                spent += (t1 - t0) + (t3 - t2)
+                tokens += len(rr)
+                sampled.append((r, len(rr)))
+                if spent >= budget_s:
+                    break
+            if spent >= budget_s:
+                break
+    reqs = sorted({r for r, _ in sampled})
+    what = (f"{tokens} decode query rows ({len(reqs)} of {wl.B} requests), all {Hkv} KV heads and candidate blocks"
+            if decode else f"{tokens} of {wl.Nq} prefill query rows (evenly spaced), all {Hkv} KV heads")
+    return {"value": tokens / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{what}: score, top-k, " + ("page table, paged decode attention" if decode else
+                                                     "per-block partials, LSE merge") + f"; {spent:.1f} s",
+            "oracle_s": spent}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the MSA path would shard "
+              "by request or KV head with no exchange; only the one-GPU share is built and timed)",
+              file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import block_sparse_long_msa_amd as msa
+    from block_sparse_long_msa_amd.pipeline import MSADecode, MSAPrefill
+    msa.load()
+    torch.cuda.set_device(0)
+
+    wl = make_workload(args.workload, args.batch)
+    decode = max(wl.q_counts) <= 16
+    t0 = time.time()
+    dev = mi.make_inputs(wl, "cuda")
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    b = msa.Batch(dev.block_table, dev.ctx_len, dev.cu_q, dev.q_pos, max(wl.q_counts))
+    P = dev.kcache.shape[0]
+    run = (MSADecode if decode else MSAPrefill)(b, wl.Hkv, wl.G, wl.D, wl.k, P)
+    flush = None
+    if not args.no_flush:
+        flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
+        flush.random_(0, 1 << 20)
+
+    def evict():                     # read-only sweep of 1 GiB
+        flush.sum(dtype=torch.int64)
+
+    # stage boundaries for per-kernel event timing
+    stages = ["score", "select", "attend"] + ([] if decode else ["merge"])
+
+    def step(evs=None):
+        for i, name in enumerate(stages):
+            if evs is not None:
+                evs[i].record()
+            if name == "score":
+                run.score(dev.q_idx, dev.kidx)
+            elif name == "select":
+                run.select()
+            elif name == "attend":
+                run.attend(dev.q, dev.kcache, dev.vcache, dev.scale)
+            else:
+                run.merge()
+        if evs is not None:
+            evs[-1].record()
+
+    for _ in range(args.warmup):
+        if flush is not None:
+            evict()
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.time()
+    for i in range(args.steps):
+        if flush is not None:
+            evict()
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.time() - wall0
+    per_stage = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(len(stages))]
+                          for i in range(args.steps)])                     # ms
+    step_ms = per_stage.sum(axis=1)
+    ms_per_step = float(step_ms.mean())
+    tokens = wl.Nq
+    value = tokens / (ms_per_step / 1e3)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # roofline of the scorer (dominant kernel) and of the attention kernel
+    score_ms = float(per_stage[:, 0].mean())
+    attend_ms = float(per_stage[:, 2].mean())
+    cand = candidate_tokens(wl)
+    sel_tok = selected_tokens(dev, run.sel, run.cnt)
+    if decode:
+        score_bytes = cand * wl.Hkv * wl.Di * 2                  # every candidate token's k_idx row, once
+        roof = {"kernel": "k_score_decode", "bound": "hbm", "achieved": score_bytes / (score_ms * 1e-3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None,
+                "algorithmic_bytes": score_bytes, "avg_ms": score_ms}
+        attn_bytes = sel_tok * wl.D * 2 * 2                      # K and V rows of the selected tokens
+        roof_attn = {"kernel": "k_attn_decode+k_lse_merge", "bound": "hbm",
+                     "achieved": attn_bytes / (attend_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "algorithmic_bytes": attn_bytes, "avg_ms": attend_ms}
+    else:
+        score_flops = 2.0 * cand * wl.Hkv * wl.Di
+        roof = {"kernel": "k_score_prefill", "bound": "mfma",
+                "achieved": score_flops / (score_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "traffic": None, "algorithmic_flops": score_flops, "avg_ms": score_ms}
+        attn_flops = 4.0 * sel_tok * wl.G * wl.D               # QK^T and PV over the selected tokens
+        roof_attn = {"kernel": "msa_sparse_attn_prefill", "bound": "mfma",
+                     "achieved": attn_flops / (attend_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "algorithmic_flops": attn_flops, "avg_ms": attend_ms}
+    for r in (roof, roof_attn):
+        r["frac"] = r["achieved"] / r["peak"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(dev, budget_s=args.cpu_budget_s)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "phase": "decode" if decode else "prefill", "requests": wl.B,
+                   "query_tokens": wl.Nq, "ctx_len": wl.ctx_lens[0] if len(set(wl.ctx_lens)) == 1 else "ragged",
+                   "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "Di": wl.Di, "top_k": wl.k, "block": wl.block,
+                   "l2_flush_between_steps": flush is not None},
+        "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "roofline_detail": [roof, roof_attn],
+        "stage_ms": {name: float(per_stage[:, i].mean()) for i, name in enumerate(stages)},
+        "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
+        "cpu_baseline": cpu,
+        "wall_s_timed": wall, "input_gen_s": gen_s,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -112,8 +112,8 @@ def msa_sparse_attn_decode(rows: int, G: int, D: int, q, k_base, v_base, page_st
                                         _stream(stream)))
 
 
-def msa_sparse_attn_prefill_workspace_size(num_queries: int, num_kv_heads: int, k: int, num_pages: int) -> int:
-    return int(load().msa_sparse_attn_prefill_workspace_size(num_queries, num_kv_heads, k, num_pages))
+def msa_sparse_attn_prefill_workspace_size(batch: Batch, num_kv_heads: int, k: int) -> int:
+    return int(load().msa_sparse_attn_prefill_workspace_size(batch.ref(), num_kv_heads, k))
 
 
 def msa_sparse_attn_prefill(batch: Batch, G: int, q, k_cache, v_cache, sel, cnt, k: int, sm_scale: float, part_o,

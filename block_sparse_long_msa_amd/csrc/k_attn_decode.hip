@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = 32 * w + 16 * sub + 4 * qd + i;
-      vr[sub][i] = (tok < valid && 8 * n < D) ? ld16(vb + (int64_t)tok * token_stride + 8 * n) : zero4();
+      vr[sub][i] = (tok < valid && 8 * n < D) ? ld16_nt(vb + (int64_t)tok * token_stride + 8 * n) : zero4();
     }
 
   f32x4 s[2];
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(
     s[sub] = fzero4();
 #pragma unroll
     for (int kw = 0; kw < KW; ++kw) {
-      const u32x4 a = (tok < valid) ? ld16(kb + (int64_t)tok * token_stride + 32 * kw + 8 * qd) : zero4();
+      const u32x4 a = (tok < valid) ? ld16_nt(kb + (int64_t)tok * token_stride + 32 * kw + 8 * qd) : zero4();
       s[sub] = mfma_bf16(a, qf[kw], s[sub]);
     }
   }

@@ -1,11 +1,375 @@
-// KV-block-major prefill attention (placeholder until the kernel lands).
+// KV-block-major sparse attention for prefill, and the {q, kv block} -> {kv block, q} remap.
+//
+// The pages (Chinese rendering of Together AI's MiniMax-M3 write-up, section
+// "KV块主序稀疏注意力减少冗余KV移动"; Russian page, third paragraph) make the KV block the outer
+// loop: each selected block is moved from HBM once and attended by every query that picked
+// it, and because a block only yields a partial output, a log-sum-exp reduction rescales and
+// sums the partials afterwards (k_lse_merge).
+//
+// Remap (a counting sort, three tiny kernels):
+//   bucket = (KV head g, request r, logical block b), ordered g-major so the query rows of one
+//   KV head (the operand re-read once per selected block) stay resident in the MALL while that
+//   head's buckets run.  count -> exclusive scan -> scatter (t, j) into the bucket lists, plus a
+//   work list of (bucket, chunk of kChunk query tokens).  Order within a bucket is not fixed,
+//   but every (t, g, j) result is computed from its own query row only, so outputs are exact
+//   and reproducible whatever the order.
+//
+// k_attn_kvbm: one workgroup per work item.  It stages block b of KV head g in LDS once -- K
+// row-major and V transposed -- then streams the chunk's query rows through it in passes of
+// 16*kNT rows per wave (rows = query tokens x G heads).  S^T = K Q^T on bf16 MFMA (tokens are
+// M, query rows are N); P never leaves registers: its bf16 values are the B operand of
+// O^T = V^T P^T because the PV contraction visits the tokens in the order the S tile already
+// holds them (token 32ks + 4qd + e for e < 4, 32ks + 16 + 4qd + e - 4 after).  The causal mask
+// (key s valid iff s <= q_pos[t] and s < ctx_len[r]) applies per query row.  Each (t, g, j)
+// gets its normalized partial output (bf16) and natural-log LSE.
+//
+// Work items are mapped XCD-aware: workgroup i runs on XCD i % 8, and the items of one XCD are
+// contiguous in the work list, so the items of one bucket share that XCD's L2 for the block.
 #include "msa_device.h"
 
 namespace msa {
-size_t prefill_workspace_bytes(int32_t Nq, int32_t Hkv, int32_t k, int32_t num_pages) { return 256; }
-hipError_t launch_attn_prefill(int, int, int, int, int, int, const int32_t*, const int32_t*, const int32_t*,
-                               const int32_t*, const void*, const void*, const void*, int, const int32_t*,
-                               const int32_t*, int, float, void*, float*, void*, hipStream_t) {
-  return hipErrorNotSupported;
+
+constexpr int kChunk = 128;  // query tokens per work item
+constexpr int kNT = 2;       // 16-row MFMA N tiles per wave per pass
+constexpr int kXcds = 8;     // MI355X: workgroups are dealt round-robin to 8 XCDs
+constexpr float kLog2eP = 1.4426950408889634f;
+constexpr float kLn2P = 0.6931471805599453f;
+
+struct PrefillWs {
+  int32_t* counts;    // [NB]
+  int32_t* cursor;    // [NB]
+  int32_t* offsets;   // [NB + 1]
+  int32_t* item_off;  // [NB + 1]; item_off[NB] = number of work items
+  int32_t* entries;   // [Nq*Hkv*k] packed t * 64 + j
+  int2* items;        // [max_items] (bucket, chunk)
+};
+
+static size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
+
+static int64_t max_items(int64_t total_entries, int64_t NB) {
+  return total_entries / kChunk + (total_entries < NB ? total_entries : NB) + 1;
 }
+
+size_t prefill_workspace_bytes(int32_t Nq, int32_t Hkv, int32_t k, int32_t B, int32_t max_blocks) {
+  const int64_t NB = (int64_t)Hkv * B * max_blocks;
+  const int64_t E = (int64_t)Nq * Hkv * k;
+  return a256(NB * 4) * 2 + a256((NB + 1) * 4) * 2 + a256(E * 4) + a256(max_items(E, NB) * 8);
+}
+
+static PrefillWs carve(void* ws, int64_t NB, int64_t E) {
+  char* p = static_cast<char*>(ws);
+  PrefillWs w;
+  w.counts = reinterpret_cast<int32_t*>(p); p += a256(NB * 4);
+  w.cursor = reinterpret_cast<int32_t*>(p); p += a256(NB * 4);
+  w.offsets = reinterpret_cast<int32_t*>(p); p += a256((NB + 1) * 4);
+  w.item_off = reinterpret_cast<int32_t*>(p); p += a256((NB + 1) * 4);
+  w.entries = reinterpret_cast<int32_t*>(p); p += a256(E * 4);
+  w.items = reinterpret_cast<int2*>(p);
+  return w;
+}
+
+__global__ void k_fill_i32(int32_t* __restrict__ a, int64_t n, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    a[i] = v;
+}
+
+// Per (t, g, j): count the entry into its bucket, or mark an empty slot's partials as absent.
+__global__ __launch_bounds__(256) void k_remap_count(int64_t E, int B, int Hkv, int k, int G, int max_blocks,
+                                                     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ sel,
+                                                     const int32_t* __restrict__ cnt, int32_t* __restrict__ counts,
+                                                     float* __restrict__ part_lse) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= E) return;
+  const int64_t tg = idx / k;
+  const int j = (int)(idx % k);
+  const int g = (int)(tg % Hkv);
+  const int t = (int)(tg / Hkv);
+  if (j < cnt[tg]) {
+    const int r = request_of(cu_q, B, t);
+    const int b = sel[idx];
+    atomicAdd(&counts[((int64_t)g * B + r) * max_blocks + b], 1);
+  } else {
+    for (int h = 0; h < G; ++h) part_lse[idx * G + h] = neg_inf();
+  }
+}
+
+// Exclusive scans of the bucket sizes and of their work-item counts (one workgroup).
+__global__ __launch_bounds__(1024) void k_remap_scan(int64_t NB, const int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ item_off) {
+  __shared__ int32_t s_a[1024], s_b[1024];
+  __shared__ int32_t carry[2];
+  const int tid = threadIdx.x;
+  if (tid == 0) { carry[0] = 0; carry[1] = 0; }
+  __syncthreads();
+  for (int64_t base = 0; base < NB; base += 1024) {
+    const int64_t i = base + tid;
+    const int32_t c = i < NB ? counts[i] : 0;
+    int32_t a = c, b = (c + kChunk - 1) / kChunk;
+    s_a[tid] = a;
+    s_b[tid] = b;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {  // Hillis-Steele inclusive scan
+      const int32_t xa = tid >= off ? s_a[tid - off] : 0;
+      const int32_t xb = tid >= off ? s_b[tid - off] : 0;
+      __syncthreads();
+      s_a[tid] += xa;
+      s_b[tid] += xb;
+      __syncthreads();
+    }
+    const int32_t ca = carry[0], cb = carry[1];
+    if (i < NB) {
+      offsets[i] = ca + s_a[tid] - a;
+      item_off[i] = cb + s_b[tid] - b;
+    }
+    __syncthreads();
+    if (tid == 1023) { carry[0] = ca + s_a[1023]; carry[1] = cb + s_b[1023]; }
+    __syncthreads();
+  }
+  if (tid == 0) { offsets[NB] = carry[0]; item_off[NB] = carry[1]; }
+}
+
+__global__ __launch_bounds__(256) void k_remap_fill(int64_t E, int B, int Hkv, int k, int max_blocks,
+                                                    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ sel,
+                                                    const int32_t* __restrict__ cnt,
+                                                    const int32_t* __restrict__ offsets, int32_t* __restrict__ cursor,
+                                                    int32_t* __restrict__ entries) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= E) return;
+  const int64_t tg = idx / k;
+  const int j = (int)(idx % k);
+  if (j >= cnt[tg]) return;
+  const int g = (int)(tg % Hkv);
+  const int t = (int)(tg / Hkv);
+  const int r = request_of(cu_q, B, t);
+  const int64_t bucket = ((int64_t)g * B + r) * max_blocks + sel[idx];
+  const int slot = offsets[bucket] + atomicAdd(&cursor[bucket], 1);
+  entries[slot] = t * 64 + j;
+}
+
+__global__ __launch_bounds__(256) void k_remap_items(int64_t NB, const int32_t* __restrict__ counts,
+                                                     const int32_t* __restrict__ item_off, int2* __restrict__ items) {
+  const int64_t bucket = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (bucket >= NB) return;
+  const int n = (counts[bucket] + kChunk - 1) / kChunk;
+  const int base = item_off[bucket];
+  for (int c = 0; c < n; ++c) items[base + c] = make_int2((int)bucket, c);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_kvbm(
+    int B, int Hkv, int G, int k, int max_blocks, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q,
+    const bf16* __restrict__ kcache, const bf16* __restrict__ vcache, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ item_off, const int2* __restrict__ items, const int32_t* __restrict__ entries,
+    int64_t NB, float scale_log2, bf16* __restrict__ part_o, float* __restrict__ part_lse) {
+  constexpr int KW = D / 32;        // 32-wide k windows over the head dimension
+  constexpr int DT = D / 16;        // 16-row d tiles of O^T
+  constexpr int KS = kBlock / 32;   // 32-token k steps of the PV contraction
+  constexpr int PAD = 8;            // LDS row padding (elements)
+  constexpr int KST = D + PAD;      // K row stride
+  constexpr int VST = kBlock + PAD; // V^T row stride
+  __shared__ __attribute__((aligned(16))) bf16 k_lds[kBlock * KST];
+  __shared__ __attribute__((aligned(16))) bf16 vt_lds[D * VST];
+
+  // XCD-aware item choice: the workgroups of one XCD take one contiguous run of items
+  const int n_items = item_off[NB];
+  const int per_xcd = (n_items + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int item = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (slot >= per_xcd || item >= n_items) return;
+  const int2 it = items[item];
+  const int64_t bucket = it.x;
+  const int g = (int)(bucket / ((int64_t)B * max_blocks));
+  const int rb = (int)(bucket % ((int64_t)B * max_blocks));
+  const int r = rb / max_blocks, b = rb % max_blocks;
+  const int e_begin = offsets[bucket] + it.y * kChunk;
+  const int e_end = min(e_begin + kChunk, offsets[bucket + 1]);
+  const int L = ctx_len[r];
+  const int page = block_table[(int64_t)r * max_blocks + b];
+  const int in_block = min(kBlock, L - b * kBlock);  // tokens of the block that exist
+  const int Hq = Hkv * G;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, qd = lane >> 4;
+
+  // ---- stage K (row-major) and V (transposed) of block b, KV head g ----
+  const bf16* kg = kcache + ((int64_t)page * kBlock * Hkv + g) * D;
+  const bf16* vg = vcache + ((int64_t)page * kBlock * Hkv + g) * D;
+  const int64_t tstride = (int64_t)Hkv * D;
+#pragma unroll
+  for (int c = 0; c < kBlock * D / 8 / 256; ++c) {
+    const int idx = tid + 256 * c, tok = idx / (D / 8), ch = idx % (D / 8);
+    const u32x4 v = tok < in_block ? ld16(kg + tok * tstride + ch * 8) : zero4();
+    st16(&k_lds[tok * KST + ch * 8], v);
+  }
+#pragma unroll
+  for (int c = 0; c < kBlock * D / 16 / 256; ++c) {  // two tokens per lane -> 32-bit transposed writes
+    const int idx = tid + 256 * c, tp = idx % (kBlock / 2), ch = idx / (kBlock / 2);
+    const int t0 = 2 * tp;
+    const u32x4 a = t0 < in_block ? ld16(vg + t0 * tstride + ch * 8) : zero4();
+    const u32x4 bb = t0 + 1 < in_block ? ld16(vg + (t0 + 1) * tstride + ch * 8) : zero4();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = (a[e] & 0xffffu) | (bb[e] << 16);           // d = 8ch + 2e
+      const uint32_t hi = (a[e] >> 16) | (bb[e] & 0xffff0000u);       // d = 8ch + 2e + 1
+      *reinterpret_cast<uint32_t*>(&vt_lds[(8 * ch + 2 * e) * VST + t0]) = lo;
+      *reinterpret_cast<uint32_t*>(&vt_lds[(8 * ch + 2 * e + 1) * VST + t0]) = hi;
+    }
+  }
+  __syncthreads();
+
+  const int rows_per_pass = 16 * kNT;          // query rows per wave per pass
+  const int tpw = rows_per_pass / G;           // query tokens per wave per pass
+  const int s_base = b * kBlock;               // absolute position of the block's first key
+
+  for (int e0 = e_begin + w * tpw; e0 < e_end; e0 += 4 * tpw) {
+    // lane's query rows: row 16nt + n of this wave's pass
+    u32x4 qf[kNT][KW];
+    int pos[kNT], tj[kNT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const int rr = 16 * nt + n, s = rr / G, h = rr % G;
+      const int e = e0 + s;
+      const bool ok = e < e_end;
+      const int packed = ok ? entries[e] : 0;
+      tj[nt] = ok ? packed : -1;
+      const int t = packed >> 6;
+      pos[nt] = ok ? q_pos[t] : -1;
+      const bf16* qrow = q + ((int64_t)t * Hq + g * G + h) * D + 8 * qd;
+      const uint32_t msk = ok ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int kw = 0; kw < KW; ++kw) qf[nt][kw] = ld16(qrow + 32 * kw) & msk;
+    }
+    // S^T[token][row] for the 128 tokens of the block
+    f32x4 sacc[kNT][8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      u32x4 a[KW];
+#pragma unroll
+      for (int kw = 0; kw < KW; ++kw) a[kw] = ld16(&k_lds[(16 * mt + n) * KST + 32 * kw + 8 * qd]);
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        f32x4 c = fzero4();
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw) c = mfma_bf16(a[kw], qf[nt][kw], c);
+        sacc[nt][mt] = c;
+      }
+    }
+    // masked softmax statistics per row (base-2 exponent)
+    float mrow[kNT], lrow[kNT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const int lim = min(pos[nt] + 1, L) - s_base;  // tokens < lim are valid for this row
+      float m = neg_inf();
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 16 * mt + 4 * qd + i;
+          const float x = tok < lim ? sacc[nt][mt][i] * scale_log2 : neg_inf();
+          sacc[nt][mt][i] = x;
+          m = fmaxf(m, x);
+        }
+      m = max_over_quads(m);
+      float l = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = m == neg_inf() ? 0.f : exp2f(sacc[nt][mt][i] - m);
+          sacc[nt][mt][i] = p;
+          l += p;
+        }
+      mrow[nt] = m;
+      lrow[nt] = sum_over_quads(l);
+    }
+    // P (bf16) as the B operand of the PV MFMA, in the S tile's own token order
+    u32x4 pb[kNT][KS];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const f32x4 lo = sacc[nt][2 * ks], hi = sacc[nt][2 * ks + 1];
+        u32x4 v;
+        v[0] = pack_bf2(lo[0], lo[1]);
+        v[1] = pack_bf2(lo[2], lo[3]);
+        v[2] = pack_bf2(hi[0], hi[1]);
+        v[3] = pack_bf2(hi[2], hi[3]);
+        pb[nt][ks] = v;
+      }
+    f32x4 oacc[kNT][DT];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[nt][dt] = fzero4();
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16* vrow = &vt_lds[(16 * dt + n) * VST + 32 * ks + 4 * qd];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        u32x4 a;
+        a[0] = lo.x; a[1] = lo.y; a[2] = hi.x; a[3] = hi.y;
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) oacc[nt][dt] = mfma_bf16(a, pb[nt][ks], oacc[nt][dt]);
+      }
+    }
+    // write normalized partials: lane holds O^T[d = 16dt + 4qd + i][row n]
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      if (tj[nt] < 0) continue;
+      const int rr = 16 * nt + n, h = rr % G;
+      const int t = tj[nt] >> 6, j = tj[nt] & 63;
+      const int64_t slot_row = (((int64_t)t * Hkv + g) * k + j) * G + h;
+      const float inv = 1.f / lrow[nt];
+      bf16* dst = part_o + slot_row * D + 4 * qd;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        uint2 v;
+        v.x = pack_bf2(oacc[nt][dt][0] * inv, oacc[nt][dt][1] * inv);
+        v.y = pack_bf2(oacc[nt][dt][2] * inv, oacc[nt][dt][3] * inv);
+        *reinterpret_cast<uint2*>(dst + 16 * dt) = v;
+      }
+      if (qd == 0) part_lse[slot_row] = (mrow[nt] + log2f(lrow[nt])) * kLn2P;
+    }
+  }
+}
+
+hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blocks, const int32_t* block_table,
+                               const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const void* q,
+                               const void* kcache, const void* vcache, const int32_t* sel, const int32_t* cnt, int k,
+                               float sm_scale, void* part_o, float* part_lse, void* workspace, hipStream_t stream) {
+  const int64_t NB = (int64_t)Hkv * B * max_blocks;
+  const int64_t E = (int64_t)Nq * Hkv * k;
+  PrefillWs ws = carve(workspace, NB, E);
+  const int fill_blocks = (int)((NB + 255) / 256 < 4096 ? (NB + 255) / 256 : 4096);
+  hipLaunchKernelGGL(k_fill_i32, dim3(fill_blocks), dim3(256), 0, stream, ws.counts, NB, 0);
+  hipLaunchKernelGGL(k_fill_i32, dim3(fill_blocks), dim3(256), 0, stream, ws.cursor, NB, 0);
+  const unsigned eb = (unsigned)((E + 255) / 256);
+  hipLaunchKernelGGL(k_remap_count, dim3(eb), dim3(256), 0, stream, E, B, Hkv, k, G, max_blocks, cu_q, sel, cnt,
+                     ws.counts, part_lse);
+  hipLaunchKernelGGL(k_remap_scan, dim3(1), dim3(1024), 0, stream, NB, ws.counts, ws.offsets, ws.item_off);
+  hipLaunchKernelGGL(k_remap_fill, dim3(eb), dim3(256), 0, stream, E, B, Hkv, k, max_blocks, cu_q, sel, cnt,
+                     ws.offsets, ws.cursor, ws.entries);
+  hipLaunchKernelGGL(k_remap_items, dim3((unsigned)((NB + 255) / 256)), dim3(256), 0, stream, NB, ws.counts,
+                     ws.item_off, ws.items);
+  // upper bound on the work items, rounded up to whole XCD rounds
+  const int64_t mi = max_items(E, NB);
+  const unsigned grid = (unsigned)(((mi + kXcds - 1) / kXcds) * kXcds);
+  const float sl2 = sm_scale * kLog2eP;
+  const bf16* qq = static_cast<const bf16*>(q);
+  const bf16* kc = static_cast<const bf16*>(kcache);
+  const bf16* vc = static_cast<const bf16*>(vcache);
+  bf16* po = static_cast<bf16*>(part_o);
+  if (D == 128)
+    hipLaunchKernelGGL(k_attn_kvbm<128>, dim3(grid), dim3(256), 0, stream, B, Hkv, G, k, max_blocks, block_table,
+                       ctx_len, q_pos, qq, kc, vc, ws.offsets, ws.item_off, ws.items, ws.entries, NB, sl2, po,
+                       part_lse);
+  else
+    hipLaunchKernelGGL(k_attn_kvbm<64>, dim3(grid), dim3(256), 0, stream, B, Hkv, G, k, max_blocks, block_table,
+                       ctx_len, q_pos, qq, kc, vc, ws.offsets, ws.item_off, ws.items, ws.entries, NB, sl2, po,
+                       part_lse);
+  return hipGetLastError();
+}
+
 }  // namespace msa

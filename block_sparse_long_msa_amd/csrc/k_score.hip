@@ -16,7 +16,34 @@
 //    scores never reach memory.
 #include "msa_device.h"
 
+#ifndef MSA_SCORE_PREFETCH
+#define MSA_SCORE_PREFETCH 2
+#endif
+
 namespace msa {
+
+// Operands of one KV head for the decode scorer: the wave's two 16-token key-index tiles and
+// the (zero-padded) query index fragments.
+template <int KW>
+struct DecodeFrags {
+  u32x4 a[2][KW];
+  u32x4 b[KW];
+};
+
+template <int DI>
+__device__ __forceinline__ void load_decode_frags(DecodeFrags<DI / 32>& f, const bf16* __restrict__ ka,
+                                                  const bf16* __restrict__ qa, int g, int Hkv, uint32_t qmask) {
+  constexpr int KW = DI / 32;
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int kw = 0; kw < KW; ++kw) f.a[sub][kw] = ld16_nt(ka + ((int64_t)(16 * sub) * Hkv + g) * DI + 32 * kw);
+#pragma unroll
+  for (int kw = 0; kw < KW; ++kw) {
+    u32x4 v = ld16(qa + (int64_t)g * DI + 32 * kw);
+    f.b[kw] = v & qmask;  // padded query columns contribute zeros, without a branch
+  }
+}
 
 template <int DI>
 __global__ __launch_bounds__(256) void k_score_decode(
@@ -24,6 +51,7 @@ __global__ __launch_bounds__(256) void k_score_decode(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q_idx,
     const bf16* __restrict__ kidx, int Hkv, float* __restrict__ scores) {
   constexpr int KW = DI / 32;
+  constexpr int PF = MSA_SCORE_PREFETCH;  // KV heads in flight ahead of the one being multiplied
   __shared__ float red[4][64][16];
   const int b = blockIdx.x, r = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, qd = lane >> 4;
@@ -31,8 +59,10 @@ __global__ __launch_bounds__(256) void k_score_decode(
 
   for (int qc = 0; qc < nq; qc += 16) {
     const int nqc = min(16, nq - qc);
-    const int my_t = q0 + qc + n;
-    const int pos = (n < nqc) ? q_pos[my_t] : -1;
+    const bool qvalid = n < nqc;
+    const int my_t = q0 + qc + (qvalid ? n : 0);  // padded lanes read a real row, then mask it
+    const int pos = qvalid ? q_pos[my_t] : -1;
+    const uint32_t qmask = qvalid ? 0xffffffffu : 0u;
     int maxpos = pos;
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1) maxpos = max(maxpos, __shfl_xor(maxpos, m, kWave));
@@ -45,37 +75,39 @@ __global__ __launch_bounds__(256) void k_score_decode(
       continue;
     }
     const int page = block_table[(int64_t)r * max_blocks + b];
-    const bf16* kb = kidx + (int64_t)page * kBlock * Hkv * DI;
+    // lane (n, qd): A rows are tokens 32w + 16sub + n, k chunk 8qd within each 32-wide window
+    const bf16* ka = kidx + ((int64_t)page * kBlock + 32 * w + n) * Hkv * DI + 8 * qd;
+    const bf16* qa = q_idx + (int64_t)my_t * Hkv * DI + 8 * qd;
     const int tok_base = b * kBlock + 32 * w + 4 * qd;
 
-#pragma unroll 2
-    for (int g = 0; g < Hkv; ++g) {
-      u32x4 qf[KW];
+    DecodeFrags<KW> ring[PF];
 #pragma unroll
-      for (int kw = 0; kw < KW; ++kw)
-        qf[kw] = (n < nqc) ? ld16(q_idx + ((int64_t)my_t * Hkv + g) * DI + 32 * kw + 8 * qd) : zero4();
-      u32x4 a[2][KW];
+    for (int p = 0; p < PF; ++p)
+      if (p < Hkv) load_decode_frags<DI>(ring[p], ka, qa, p, Hkv, qmask);
+
+    for (int g0 = 0; g0 < Hkv; g0 += PF) {
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int tok = 32 * w + 16 * sub + n;
+      for (int p = 0; p < PF; ++p) {
+        const int g = g0 + p;
+        if (g < Hkv) {
+          const DecodeFrags<KW> cur = ring[p];
+          if (g + PF < Hkv) load_decode_frags<DI>(ring[p], ka, qa, g + PF, Hkv, qmask);
+          float m = neg_inf();
 #pragma unroll
-        for (int kw = 0; kw < KW; ++kw)
-          a[sub][kw] = ld16(kb + ((int64_t)tok * Hkv + g) * DI + 32 * kw + 8 * qd);
-      }
-      float m = neg_inf();
+          for (int sub = 0; sub < 2; ++sub) {
+            f32x4 acc = fzero4();
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        f32x4 acc = fzero4();
+            for (int kw = 0; kw < KW; ++kw) acc = mfma_bf16(cur.a[sub][kw], cur.b[kw], acc);
 #pragma unroll
-        for (int kw = 0; kw < KW; ++kw) acc = mfma_bf16(a[sub][kw], qf[kw], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = tok_base + 16 * sub + i;
-          if (s <= pos && s < L) m = fmaxf(m, acc[i]);
+            for (int i = 0; i < 4; ++i) {
+              const int s = tok_base + 16 * sub + i;
+              m = (s <= pos && s < L) ? fmaxf(m, acc[i]) : m;
+            }
+          }
+          m = max_over_quads(m);
+          if (qd == 0) red[w][g][n] = m;
         }
       }
-      m = max_over_quads(m);
-      if (qd == 0) red[w][g][n] = m;
     }
     __syncthreads();
     for (int e = tid; e < nqc * Hkv; e += 256) {

@@ -28,12 +28,11 @@ hipError_t launch_lse_merge_bf16(int64_t rows, int parts, int G, int D, const vo
                                  void* out, float* lse_out, hipStream_t stream);
 hipError_t launch_lse_merge_f32(int64_t rows, int parts, int G, int D, const float* part_o, const float* part_lse,
                                 void* out, float* lse_out, hipStream_t stream);
-size_t prefill_workspace_bytes(int32_t Nq, int32_t Hkv, int32_t k, int32_t num_pages);
+size_t prefill_workspace_bytes(int32_t Nq, int32_t Hkv, int32_t k, int32_t B, int32_t max_blocks);
 hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blocks, const int32_t* block_table,
                                const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const void* q,
-                               const void* kcache, const void* vcache, int num_pages, const int32_t* sel,
-                               const int32_t* cnt, int k, float sm_scale, void* part_o, float* part_lse,
-                               void* workspace, hipStream_t stream);
+                               const void* kcache, const void* vcache, const int32_t* sel, const int32_t* cnt, int k,
+                               float sm_scale, void* part_o, float* part_lse, void* workspace, hipStream_t stream);
 }  // namespace msa
 
 namespace {
@@ -220,10 +219,11 @@ msa_status msa_sparse_attn_decode(int32_t rows, int32_t G, int32_t D, const void
                   "msa_sparse_attn_decode merge launch");
 }
 
-size_t msa_sparse_attn_prefill_workspace_size(int32_t num_queries, int32_t num_kv_heads, int32_t k,
-                                              int32_t num_pages) {
-  if (num_queries < 0 || num_kv_heads <= 0 || k <= 0 || num_pages <= 0) return 0;
-  return msa::prefill_workspace_bytes(num_queries, num_kv_heads, k, num_pages);
+size_t msa_sparse_attn_prefill_workspace_size(const msa_batch* batch, int32_t num_kv_heads, int32_t k) {
+  if (!batch || batch->num_queries < 0 || batch->num_requests <= 0 || batch->max_blocks <= 0 || num_kv_heads <= 0 ||
+      k <= 0)
+    return 0;
+  return msa::prefill_workspace_bytes(batch->num_queries, num_kv_heads, k, batch->num_requests, batch->max_blocks);
 }
 
 msa_status msa_sparse_attn_prefill(const msa_batch* batch, int32_t G, const void* q, msa_cache k_cache,
@@ -249,14 +249,15 @@ msa_status msa_sparse_attn_prefill(const msa_batch* batch, int32_t G, const void
   MSA_REQUIRE((int64_t)batch->num_queries * k_cache.num_heads * k <= 0x7fffffffLL, MSA_ERR_UNSUPPORTED,
               "num_queries*Hkv*k must fit in int32");
   MSA_REQUIRE((int64_t)batch->num_queries < (1LL << 25), MSA_ERR_UNSUPPORTED, "num_queries must be < 2^25");
-  const size_t need = msa_sparse_attn_prefill_workspace_size(batch->num_queries, k_cache.num_heads, k,
-                                                             k_cache.num_pages);
+  MSA_REQUIRE((int64_t)k_cache.num_heads * batch->num_requests * batch->max_blocks <= 0x7fffffffLL,
+              MSA_ERR_UNSUPPORTED, "num_kv_heads*num_requests*max_blocks must fit in int32");
+  const size_t need = msa_sparse_attn_prefill_workspace_size(batch, k_cache.num_heads, k);
   MSA_REQUIRE(workspace_bytes >= need, MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
               workspace_bytes);
   return from_hip(msa::launch_attn_prefill(batch->num_requests, batch->num_queries, k_cache.num_heads, G,
                                            k_cache.head_dim, batch->max_blocks, batch->block_table, batch->ctx_len,
-                                           batch->cu_q, batch->q_pos, q, k_cache.data, v_cache.data,
-                                           k_cache.num_pages, sel, cnt, k, sm_scale, part_o, part_lse, workspace,
+                                           batch->cu_q, batch->q_pos, q, k_cache.data, v_cache.data, sel, cnt, k,
+                                           sm_scale, part_o, part_lse, workspace,
                                            reinterpret_cast<hipStream_t>(stream)),
                   "msa_sparse_attn_prefill launch");
 }

@@ -28,6 +28,11 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(l
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Streaming load for data read exactly once (non-temporal hint): keeps it from displacing
+// reused lines in L2 / the MALL and runs closer to the HBM peak than ordinary loads.
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 

@@ -60,7 +60,7 @@ class MSAPrefill:
         self.part_lse = torch.empty((Nq, Hkv, k, G), dtype=torch.float32, device=device)
         self.out = torch.empty((Nq, Hkv * G, D), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((Nq, Hkv * G), dtype=torch.float32, device=device)
-        self.ws = torch.empty((msa_sparse_attn_prefill_workspace_size(Nq, Hkv, k, num_pages),), dtype=torch.uint8,
+        self.ws = torch.empty((msa_sparse_attn_prefill_workspace_size(batch, Hkv, k),), dtype=torch.uint8,
                               device=device)
 
     def score(self, q_idx, kidx, stream=None):

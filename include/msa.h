@@ -148,8 +148,8 @@ msa_status msa_sparse_attn_prefill(const msa_batch* batch, int32_t G, const void
                                    msa_cache v_cache, const int32_t* sel, const int32_t* cnt, int32_t k,
                                    float sm_scale, void* part_o, float* part_lse, void* workspace,
                                    size_t workspace_bytes, msa_stream_t stream);
-size_t msa_sparse_attn_prefill_workspace_size(int32_t num_queries, int32_t num_kv_heads, int32_t k,
-                                              int32_t num_pages);
+/* Workspace bytes for msa_sparse_attn_prefill on this batch (0 for invalid arguments). */
+size_t msa_sparse_attn_prefill_workspace_size(const msa_batch* batch, int32_t num_kv_heads, int32_t k);
 
 /* Log-sum-exp reduction of per-block partials (section "KV块主序稀疏注意力减少冗余KV移动"):
  *   LSE = log sum_j exp(lse_j),  O = sum_j exp(lse_j - LSE) * O_j, over the parts with

@@ -1,0 +1,81 @@
+"""GPU parity of the prefill path (GEMM scorer, top-k, remap + KV-block-major attention, LSE merge)
+against the CPU oracle on identical seeded inputs.
+
+Bars as for decode; the per-block partials (bf16) are compared slot by slot with the oracle's
+block_partials on the GPU's selection, and the merged output with the oracle's one softmax over
+the union of the selected blocks.
+"""
+import numpy as np
+import pytest
+
+import msa_inputs as mi
+import oracle
+from _gpu import announce, batch, host, prefill, scores, setup, topk
+from _helpers import assert_attn_close, np_inputs, selection_excused
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "tiny_prefill_2k": None,   # the 2048-token workload itself
+    "ragged_multi_request": dict(ctx=[700, 300, 1000], nq=[300, 300, 129], Hq=16, Hkv=2, D=128, Di=128, k=5),
+    "chunk_over_prefix": dict(ctx=[2000], nq=[1000], Hq=32, Hkv=4, D=128, Di=64, k=6),
+    "g16_d64": dict(ctx=[900, 520], nq=[400, 130], Hq=32, Hkv=2, D=64, Di=128, k=3),
+    "g1_d128": dict(ctx=[640], nq=[640], Hq=4, Hkv=4, D=128, Di=128, k=2),
+    "g2_k_over_candidates": dict(ctx=[400, 129], nq=[250, 129], Hq=4, Hkv=2, D=64, Di=64, k=8),
+}
+
+
+def _wl(name, seed=31):
+    if CASES[name] is None:
+        return mi.tiny_prefill()
+    c = dict(CASES[name])
+    ctx, nq = c.pop("ctx"), c.pop("nq")
+    return mi.small_workload(ctx, nq, seed=seed, **c)
+
+
+def _run(dev):
+    b = batch(dev)
+    s = scores(dev, b)
+    sel, cnt = topk(dev, b, s)
+    po, pl, out, lse = prefill(dev, b, sel, cnt)
+    return s, sel, cnt, po, pl, out, lse
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_prefill_path_matches_oracle(name):
+    announce("prefill", name)
+    dev, cpu = setup(_wl(name))
+    x = np_inputs(cpu)
+    wl = dev.wl
+    s, sel, cnt, po, pl, out, lse = [host(t) for t in _run(dev)]
+
+    ref_s = oracle.index_scores(x.q_idx, x.kidx, x.block_table, x.ctx_len, x.q_req, x.q_pos, wl.block)
+    assert np.array_equal(np.isneginf(s), np.isneginf(ref_s)), "candidate masks differ"
+    fin = np.isfinite(ref_s)
+    assert np.abs(s[fin] - ref_s[fin]).max() <= 1e-2
+
+    o_sel, o_cnt = oracle.topk_blocks(s.astype(np.float64), x.q_pos, wl.block, wl.k)
+    assert np.array_equal(sel, o_sel) and np.array_equal(cnt, o_cnt), "top-k differs on identical scores"
+    r_sel, r_cnt = oracle.topk_blocks(ref_s, x.q_pos, wl.block, wl.k)
+    selection_excused(sel, cnt, r_sel, r_cnt, ref_s, wl.k)
+
+    ref_po, ref_pl = oracle.block_partials(x.q, x.kcache, x.vcache, x.block_table, x.ctx_len, x.q_req, x.q_pos,
+                                           sel, cnt, wl.block, x.scale)
+    present = np.arange(wl.k)[None, None, :] < cnt[:, :, None]            # [Nq, Hkv, k]
+    assert np.all(np.isneginf(pl[~present])), "empty slots must carry lse = -inf"
+    assert_attn_close(po[present], ref_po[present], what="per-block partials")
+    assert np.abs(pl[present] - ref_pl[present]).max() <= 1e-3
+
+    ref_o, ref_l = oracle.sparse_attention(x.q, x.kcache, x.vcache, x.block_table, x.ctx_len, x.q_req, x.q_pos,
+                                           sel, cnt, wl.block, x.scale)
+    assert_attn_close(out, ref_o, what="merged output")
+    assert np.abs(lse - ref_l).max() <= 1e-3
+
+
+def test_prefill_is_deterministic():
+    announce("prefill determinism")
+    dev, _ = setup(_wl("ragged_multi_request", seed=8))
+    a = [host(t) for t in _run(dev)]
+    b = [host(t) for t in _run(dev)]
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
