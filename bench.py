@@ -163,11 +163,11 @@ def main():
     run = (MSADecode if decode else MSAPrefill)(b, wl.Hkv, wl.G, wl.D, wl.k, P)
     flush = None
     if not args.no_flush:
-        flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
-        flush.random_(0, 1 << 20)
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        flush.fill_(1.0)
 
-    def evict():                     # read-only sweep of 1 GiB
-        flush.sum(dtype=torch.int64)
+    def evict():                     # read-only sweep of 1 GiB (one reduction kernel, scalar result)
+        flush.sum()
 
     # stage boundaries for per-kernel event timing
     stages = ["score", "select", "attend"] + ([] if decode else ["merge"])

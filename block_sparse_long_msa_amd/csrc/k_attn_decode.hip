@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void k_attn_decode(
   for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float p = (m == neg_inf()) ? 0.f : exp2f(s[sub][i] - m);
+      const float p = (m == neg_inf()) ? 0.f : fast_exp2(s[sub][i] - m);
       s[sub][i] = p;
       l += p;
     }
@@ -129,12 +129,12 @@ __global__ __launch_bounds__(256) void k_attn_decode(
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
       const float mw = sm_m[ww][h];
-      const float f = (mw == neg_inf()) ? 0.f : exp2f(mw - M);
+      const float f = (mw == neg_inf()) ? 0.f : fast_exp2(mw - M);
       num += f * sm_o[ww][h][d];
       den += f * sm_l[ww][h];
     }
     ws_o[(part * G + h) * D + d] = num / den;
-    if (d == 0) ws_lse[part * G + h] = (M + log2f(den)) * kLn2;
+    if (d == 0) ws_lse[part * G + h] = (M + fast_log2(den)) * kLn2;
   }
 }
 

@@ -155,21 +155,30 @@ __global__ __launch_bounds__(256) void k_remap_items(int64_t NB, const int32_t* 
   for (int c = 0; c < n; ++c) items[base + c] = make_int2((int)bucket, c);
 }
 
+// V^T in LDS: row d holds the block's 128 tokens in 4-token (8-byte) chunks; chunk c of row d is
+// stored at chunk position c ^ h(d), h(d) = ((d >> 3) & 3) * 4 + (d & 3).  The 16 lanes that read
+// one chunk index from the 16 rows 8a + b (a, b < 4) of a PV tile then hit 16 distinct chunk
+// positions, i.e. 16 distinct 8-byte bank pairs: no conflicts.
+__device__ __forceinline__ int vt_swz(int d, int tok) {
+  const int h = (((d >> 3) & 3) << 2) | (d & 3);
+  return ((((tok >> 2) ^ h)) << 2) | (tok & 3);
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_kvbm(
+__global__ __launch_bounds__(256, 2) void k_attn_kvbm(
     int B, int Hkv, int G, int k, int max_blocks, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q,
     const bf16* __restrict__ kcache, const bf16* __restrict__ vcache, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ item_off, const int2* __restrict__ items, const int32_t* __restrict__ entries,
     int64_t NB, float scale_log2, bf16* __restrict__ part_o, float* __restrict__ part_lse) {
   constexpr int KW = D / 32;        // 32-wide k windows over the head dimension
-  constexpr int DT = D / 16;        // 16-row d tiles of O^T
   constexpr int KS = kBlock / 32;   // 32-token k steps of the PV contraction
   constexpr int PAD = 8;            // LDS row padding (elements)
   constexpr int KST = D + PAD;      // K row stride
-  constexpr int VST = kBlock + PAD; // V^T row stride
+  constexpr int VST = kBlock;       // V^T row stride; 4-token chunks XOR-swizzled per row (vt_chunk)
   __shared__ __attribute__((aligned(16))) bf16 k_lds[kBlock * KST];
   __shared__ __attribute__((aligned(16))) bf16 vt_lds[D * VST];
+  __shared__ int s_tj[kChunk], s_pos[kChunk];
 
   // XCD-aware item choice: the workgroups of one XCD take one contiguous run of items
   const int n_items = item_off[NB];
@@ -211,8 +220,9 @@ __global__ __launch_bounds__(256) void k_attn_kvbm(
     for (int e = 0; e < 4; ++e) {
       const uint32_t lo = (a[e] & 0xffffu) | (bb[e] << 16);           // d = 8ch + 2e
       const uint32_t hi = (a[e] >> 16) | (bb[e] & 0xffff0000u);       // d = 8ch + 2e + 1
-      *reinterpret_cast<uint32_t*>(&vt_lds[(8 * ch + 2 * e) * VST + t0]) = lo;
-      *reinterpret_cast<uint32_t*>(&vt_lds[(8 * ch + 2 * e + 1) * VST + t0]) = hi;
+      const int d0 = 8 * ch + 2 * e;
+      *reinterpret_cast<uint32_t*>(&vt_lds[d0 * VST + vt_swz(d0, t0)]) = lo;
+      *reinterpret_cast<uint32_t*>(&vt_lds[(d0 + 1) * VST + vt_swz(d0 + 1, t0)]) = hi;
     }
   }
   __syncthreads();
@@ -220,66 +230,108 @@ __global__ __launch_bounds__(256) void k_attn_kvbm(
   const int rows_per_pass = 16 * kNT;          // query rows per wave per pass
   const int tpw = rows_per_pass / G;           // query tokens per wave per pass
   const int s_base = b * kBlock;               // absolute position of the block's first key
+  const int n_e = e_end - e_begin;             // query tokens of this work item
 
-  for (int e0 = e_begin + w * tpw; e0 < e_end; e0 += 4 * tpw) {
-    // lane's query rows: row 16nt + n of this wave's pass
+  // the item's (t, j) entries and query positions, once, in LDS
+  for (int i = tid; i < n_e; i += 256) {
+    const int packed = entries[e_begin + i];
+    s_tj[i] = packed;
+    s_pos[i] = q_pos[packed >> 6];
+  }
+  __syncthreads();
+
+  // query fragments of one pass, prefetched a pass ahead
+  struct PassQ {
     u32x4 qf[kNT][KW];
     int pos[kNT], tj[kNT];
+  };
+  auto load_pass = [&](PassQ& P, int lb) {
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
-      const int rr = 16 * nt + n, s = rr / G, h = rr % G;
-      const int e = e0 + s;
-      const bool ok = e < e_end;
-      const int packed = ok ? entries[e] : 0;
-      tj[nt] = ok ? packed : -1;
-      const int t = packed >> 6;
-      pos[nt] = ok ? q_pos[t] : -1;
-      const bf16* qrow = q + ((int64_t)t * Hq + g * G + h) * D + 8 * qd;
+      const int rr = 16 * nt + n, sl = rr / G, h = rr % G;
+      const int li = lb + sl;
+      const bool ok = li < n_e;
+      const int packed = ok ? s_tj[li] : 0;
+      P.tj[nt] = ok ? packed : -1;
+      P.pos[nt] = ok ? s_pos[li] : -1;
+      const bf16* qrow = q + ((int64_t)(packed >> 6) * Hq + g * G + h) * D + 8 * qd;
       const uint32_t msk = ok ? 0xffffffffu : 0u;
 #pragma unroll
-      for (int kw = 0; kw < KW; ++kw) qf[nt][kw] = ld16(qrow + 32 * kw) & msk;
+      for (int kw = 0; kw < KW; ++kw) P.qf[nt][kw] = ld16(qrow + 32 * kw) & msk;
     }
-    // S^T[token][row] for the 128 tokens of the block
+  };
+  PassQ nxt;
+  if (w * tpw < n_e) load_pass(nxt, w * tpw);
+
+  for (int lb = w * tpw; lb < n_e; lb += 4 * tpw) {
+    const PassQ cur = nxt;
+    if (lb + 4 * tpw < n_e) load_pass(nxt, lb + 4 * tpw);
+    const auto& qf = cur.qf;
+    const int* pos = cur.pos;
+    const int* tj = cur.tj;
+    // S^T[token][row] for the 128 tokens of the block; K fragments read one tile ahead
     f32x4 sacc[kNT][8];
+    u32x4 a_cur[KW];
+#pragma unroll
+    for (int kw = 0; kw < KW; ++kw) a_cur[kw] = ld16(&k_lds[n * KST + 32 * kw + 8 * qd]);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-      u32x4 a[KW];
+      u32x4 a_nxt[KW];
+      if (mt < 7) {
 #pragma unroll
-      for (int kw = 0; kw < KW; ++kw) a[kw] = ld16(&k_lds[(16 * mt + n) * KST + 32 * kw + 8 * qd]);
+        for (int kw = 0; kw < KW; ++kw) a_nxt[kw] = ld16(&k_lds[(16 * (mt + 1) + n) * KST + 32 * kw + 8 * qd]);
+      }
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
         f32x4 c = fzero4();
 #pragma unroll
-        for (int kw = 0; kw < KW; ++kw) c = mfma_bf16(a[kw], qf[nt][kw], c);
+        for (int kw = 0; kw < KW; ++kw) c = mfma_bf16(a_cur[kw], qf[nt][kw], c);
         sacc[nt][mt] = c;
       }
+      if (mt < 7) {
+#pragma unroll
+        for (int kw = 0; kw < KW; ++kw) a_cur[kw] = a_nxt[kw];
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // masked softmax statistics per row (base-2 exponent)
+    // softmax statistics per row: m = max of the raw logits, p = 2^(s*scale*log2e - m*scale*log2e).
+    // Rows past the chunk end have lim <= 0 and come out all-masked; they are never stored.
+    int lim[kNT];
+    bool full = true;
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      lim[nt] = min(pos[nt] + 1, L) - s_base;  // tokens < lim are valid for this row
+      full = full && lim[nt] >= kBlock;
+    }
+    full = __ballot(!full) == 0;  // wave-uniform: no row of this pass needs masking
+    if (!full) {
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * mt + 4 * qd + i >= lim[nt]) sacc[nt][mt][i] = neg_inf();
+    }
     float mrow[kNT], lrow[kNT];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
-      const int lim = min(pos[nt] + 1, L) - s_base;  // tokens < lim are valid for this row
       float m = neg_inf();
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = 16 * mt + 4 * qd + i;
-          const float x = tok < lim ? sacc[nt][mt][i] * scale_log2 : neg_inf();
-          sacc[nt][mt][i] = x;
-          m = fmaxf(m, x);
-        }
+        m = fmaxf(fmaxf(m, fmaxf(sacc[nt][mt][0], sacc[nt][mt][1])), fmaxf(sacc[nt][mt][2], sacc[nt][mt][3]));
       m = max_over_quads(m);
+      const float mb = (m == neg_inf()) ? 0.f : m * scale_log2;
       float l = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = m == neg_inf() ? 0.f : exp2f(sacc[nt][mt][i] - m);
+          const float p = fast_exp2(__builtin_fmaf(sacc[nt][mt][i], scale_log2, -mb));
           sacc[nt][mt][i] = p;
           l += p;
         }
-      mrow[nt] = m;
+      mrow[nt] = mb;
       lrow[nt] = sum_over_quads(l);
     }
     // P (bf16) as the B operand of the PV MFMA, in the S tile's own token order
@@ -296,41 +348,50 @@ __global__ __launch_bounds__(256) void k_attn_kvbm(
         v[3] = pack_bf2(hi[2], hi[3]);
         pb[nt][ks] = v;
       }
-    f32x4 oacc[kNT][DT];
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[nt][dt] = fzero4();
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16* vrow = &vt_lds[(16 * dt + n) * VST + 32 * ks + 4 * qd];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-        u32x4 a;
-        a[0] = lo.x; a[1] = lo.y; a[2] = hi.x; a[3] = hi.y;
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) oacc[nt][dt] = mfma_bf16(a, pb[nt][ks], oacc[nt][dt]);
-      }
-    }
-    // write normalized partials: lane holds O^T[d = 16dt + 4qd + i][row n]
+    // output slots of this lane's rows
+    int64_t orow[kNT];
+    float inv[kNT];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
-      if (tj[nt] < 0) continue;
       const int rr = 16 * nt + n, h = rr % G;
       const int t = tj[nt] >> 6, j = tj[nt] & 63;
-      const int64_t slot_row = (((int64_t)t * Hkv + g) * k + j) * G + h;
-      const float inv = 1.f / lrow[nt];
-      bf16* dst = part_o + slot_row * D + 4 * qd;
+      orow[nt] = (((int64_t)t * Hkv + g) * k + j) * G + h;
+      inv[nt] = 1.f / lrow[nt];
+      if (tj[nt] >= 0 && qd == 0) part_lse[orow[nt]] = (mrow[nt] + fast_log2(lrow[nt])) * kLn2P;
+    }
+    // O^T = V^T P^T, one pair of 16-row d tiles at a time.  Tile rows are permuted so that lane
+    // (n, qd) ends with d = 32u + 8qd .. 32u + 8qd + 7 of its row: row m = 4q + i of tile 2u + x
+    // holds d = 32u + 8q + 4x + i.  Each lane then stores 16 contiguous bytes per pair.
+#pragma unroll 1
+    for (int u = 0; u < D / 32; ++u) {
+      f32x4 o[kNT][2];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        uint2 v;
-        v.x = pack_bf2(oacc[nt][dt][0] * inv, oacc[nt][dt][1] * inv);
-        v.y = pack_bf2(oacc[nt][dt][2] * inv, oacc[nt][dt][3] * inv);
-        *reinterpret_cast<uint2*>(dst + 16 * dt) = v;
+      for (int nt = 0; nt < kNT; ++nt) { o[nt][0] = fzero4(); o[nt][1] = fzero4(); }
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int drow = 32 * u + 8 * (n >> 2) + 4 * x + (n & 3);  // V^T row supplied as A row m = n
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16* vrow = &vt_lds[drow * VST];
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + vt_swz(drow, 32 * ks + 4 * qd));
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + vt_swz(drow, 32 * ks + 16 + 4 * qd));
+          u32x4 a;
+          a[0] = lo.x; a[1] = lo.y; a[2] = hi.x; a[3] = hi.y;
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) o[nt][x] = mfma_bf16(a, pb[nt][ks], o[nt][x]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (qd == 0) part_lse[slot_row] = (mrow[nt] + log2f(lrow[nt])) * kLn2P;
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        if (tj[nt] < 0) continue;
+        u32x4 v;
+        v[0] = pack_bf2(o[nt][0][0] * inv[nt], o[nt][0][1] * inv[nt]);
+        v[1] = pack_bf2(o[nt][0][2] * inv[nt], o[nt][0][3] * inv[nt]);
+        v[2] = pack_bf2(o[nt][1][0] * inv[nt], o[nt][1][1] * inv[nt]);
+        v[3] = pack_bf2(o[nt][1][2] * inv[nt], o[nt][1][3] * inv[nt]);
+        st16(part_o + orow[nt] * D + 32 * u + 8 * qd, v);
+      }
     }
   }
 }

@@ -16,15 +16,13 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
 __device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// float -> bf16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even: one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
@@ -63,6 +61,11 @@ __device__ __forceinline__ float sum_over_quads(float v) {
 }
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// 2^x and log2(x) as single v_exp_f32 / v_log_f32 (results that would be denormal flush to 0,
+// which softmax weights can afford; exp2(-inf) = 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Order-preserving map of a float to uint32 (-0 is folded onto +0 so equal scores tie).
 __device__ __forceinline__ uint32_t order_key(float f) {
