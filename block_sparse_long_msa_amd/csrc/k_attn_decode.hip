@@ -138,49 +138,71 @@ __global__ __launch_bounds__(256) void k_attn_decode(
   }
 }
 
-// One wavefront per row: all G*D outputs of the row, 8 consecutive elements per lane step.
+// One wavefront per row.  The row's parts*G log-sum-exps go to LDS and become normalized
+// weights w[j][h] = exp(lse_j - LSE) once; then every lane accumulates its 8-element chunks over
+// the parts with independent 16-byte loads (absent parts have weight 0 and are not read).
+constexpr int kMergeMaxPG = 64 * 16;  // parts * G
+
 template <typename TIn>
 __global__ __launch_bounds__(256) void k_lse_merge(int64_t rows, int parts, int G, int D,
                                                    const TIn* __restrict__ part_o, const float* __restrict__ part_lse,
                                                    bf16* __restrict__ out, float* __restrict__ lse_out) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ float s_w[4][kMergeMaxPG];
+  __shared__ float s_lse[4][16];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wv;
   if (row >= rows) return;
-  const int GD = G * D;
-  const float* pl = part_lse + row * parts * G;
-  for (int c = lane; c < GD / 8; c += kWave) {
-    const int h = (8 * c) / D;
+  const int PG = parts * G, GD = G * D;
+  float* w = s_w[wv];
+  const float* pl = part_lse + row * PG;
+  for (int i = lane; i < PG; i += kWave) w[i] = pl[i];
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  if (lane < G) {  // per head: LSE and the normalization
     float M = neg_inf();
-    for (int j = 0; j < parts; ++j) M = fmaxf(M, pl[j * G + h]);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < parts; ++j) M = fmaxf(M, w[j * G + lane]);
     float den = 0.f;
     for (int j = 0; j < parts; ++j) {
-      const float lj = pl[j * G + h];
-      if (lj == neg_inf()) continue;
-      const float wgt = __expf(lj - M);
-      den += wgt;
-      const int64_t off = ((row * parts + j) * G) * (int64_t)D + 8 * c;
-      if constexpr (sizeof(TIn) == 2) {
-        const u32x4 v = ld16(part_o + off);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += wgt * __uint_as_float(v[e] << 16);
-          acc[2 * e + 1] += wgt * __uint_as_float(v[e] & 0xffff0000u);
-        }
-      } else {
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(part_o + off);
-        const f32x4 v1 = *reinterpret_cast<const f32x4*>(part_o + off + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { acc[e] += wgt * v0[e]; acc[4 + e] += wgt * v1[e]; }
-      }
+      const float lj = w[j * G + lane];
+      den += lj == neg_inf() ? 0.f : __expf(lj - M);
     }
     const float inv = 1.f / den;
+    for (int j = 0; j < parts; ++j) {
+      const float lj = w[j * G + lane];
+      w[j * G + lane] = lj == neg_inf() ? 0.f : __expf(lj - M) * inv;
+    }
+    s_lse[wv][lane] = M + __logf(den);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  for (int c = lane; c < GD / 8; c += kWave) {
+    const int h = (8 * c) / D;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const TIn* src = part_o + (row * parts) * (int64_t)GD + 8 * c;
+#pragma unroll 8
+    for (int j = 0; j < parts; ++j) {
+      const float wj = w[j * G + h];
+      if (wj == 0.f) continue;  // absent part: never read
+      if constexpr (sizeof(TIn) == 2) {
+        const u32x4 v = ld16(src + (int64_t)j * GD);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += wj * __uint_as_float(v[e] << 16);
+          acc[2 * e + 1] += wj * __uint_as_float(v[e] & 0xffff0000u);
+        }
+      } else {
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(src + (int64_t)j * GD);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + (int64_t)j * GD + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { acc[e] += wj * v0[e]; acc[4 + e] += wj * v1[e]; }
+      }
+    }
     u32x4 o;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = pack_bf2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf2(acc[2 * e], acc[2 * e + 1]);
     st16(out + (row * G) * (int64_t)D + 8 * c, o);
-    if (lse_out && (8 * c) % D == 0) lse_out[row * G + h] = M + __logf(den);
   }
+  if (lse_out && lane < G) lse_out[row * G + lane] = s_lse[wv][lane];
 }
 
 hipError_t launch_attn_decode(int rows, int G, int D, const void* q, const void* kview, const void* vview,

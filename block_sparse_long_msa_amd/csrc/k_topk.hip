@@ -122,6 +122,7 @@ __global__ __launch_bounds__(64) void k_topk(int B, int Hkv, int max_blocks, con
 
 // Decode sparse page table over the strided view (Chinese page, section "MSA需要新的分页注意力集成"):
 // row rho = t*Hkv + g, page_table[rho, j] = block_table[r, sel[t,g,j]] * 128 * Hkv + g.
+// One wavefront per row; lane j handles slot j (k <= 64), row_len is a wave sum.
 __global__ __launch_bounds__(256) void k_page_table(int rows, int B, int Hkv, int max_blocks,
                                                     const int32_t* __restrict__ block_table,
                                                     const int32_t* __restrict__ ctx_len,
@@ -129,23 +130,23 @@ __global__ __launch_bounds__(256) void k_page_table(int rows, int B, int Hkv, in
                                                     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
                                                     int k, int32_t* __restrict__ page_table,
                                                     int32_t* __restrict__ row_len) {
-  const int rho = blockIdx.x * blockDim.x + threadIdx.x;
+  const int rho = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int j = threadIdx.x & 63;
   if (rho >= rows) return;
   const int t = rho / Hkv, g = rho % Hkv;
   const int r = request_of(cu_q, B, t);
   const int lim = min(q_pos[t] + 1, ctx_len[r]);  // tokens s < lim are valid
   const int c = cnt[rho];
-  int len = 0;
-  for (int j = 0; j < k; ++j) {
-    int v = -1;
-    if (j < c) {
-      const int bl = sel[(int64_t)rho * k + j];
-      v = block_table[(int64_t)r * max_blocks + bl] * (kBlock * Hkv) + g;
-      len += min(kBlock, lim - bl * kBlock);
-    }
-    page_table[(int64_t)rho * k + j] = v;
+  int v = -1, len = 0;
+  if (j < c) {
+    const int bl = sel[(int64_t)rho * k + j];
+    v = block_table[(int64_t)r * max_blocks + bl] * (kBlock * Hkv) + g;
+    len = min(kBlock, lim - bl * kBlock);
   }
-  row_len[rho] = len;
+  if (j < k) page_table[(int64_t)rho * k + j] = v;
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) len += __shfl_xor(len, m, kWave);
+  if (j == 0) row_len[rho] = len;
 }
 
 hipError_t launch_topk(int B, int Nq, int Hkv, int max_blocks, const int32_t* cu_q, const int32_t* q_pos,
@@ -159,7 +160,7 @@ hipError_t launch_page_table(int B, int Nq, int Hkv, int max_blocks, const int32
                              const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const int32_t* sel,
                              const int32_t* cnt, int k, int32_t* page_table, int32_t* row_len, hipStream_t stream) {
   const int rows = Nq * Hkv;
-  hipLaunchKernelGGL(k_page_table, dim3((rows + 255) / 256), dim3(256), 0, stream, rows, B, Hkv, max_blocks,
+  hipLaunchKernelGGL(k_page_table, dim3((rows + 3) / 4), dim3(256), 0, stream, rows, B, Hkv, max_blocks,
                      block_table, ctx_len, cu_q, q_pos, sel, cnt, k, page_table, row_len);
   return hipGetLastError();
 }

@@ -24,6 +24,9 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// One float -> bf16 bits (round to nearest even).
+__device__ __forceinline__ uint32_t f2bf_bits(float f) { return pack_bf2(f, 0.f) & 0xffffu; }
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 // Streaming load for data read exactly once (non-temporal hint): keeps it from displacing
