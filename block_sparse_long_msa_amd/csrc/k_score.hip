@@ -119,6 +119,125 @@ __global__ __launch_bounds__(256) void k_score_decode(
   }
 }
 
+// LDS-staged decode scorer, used when one 16-token slice of a page (16 * Hkv * Di * 2 bytes) fits a
+// 32 KiB stage, i.e. Hkv * Di <= 1024.  The page is streamed with fully coalesced 16-byte
+// non-temporal loads (each wave instruction reads 1 KiB of consecutive bytes), two slices ahead in
+// registers, and stored into a double-buffered LDS stage whose token rows are padded by 16 bytes so
+// that the MFMA operand reads (16 token rows, same column) are bank-conflict free.  Wave w owns KV
+// heads w, w+4, ...: it reads their operands from LDS and keeps their running block max in
+// registers, so no cross-wave reduction is needed.
+constexpr int kStageBytes = 32768;
+constexpr int kStageLdsBytes = 16 * 16 + kStageBytes;  // + 16 B pad per token row
+constexpr int kStagePF = 2;                            // slices in flight in registers
+
+template <int DI>
+__global__ __launch_bounds__(256, 2) void k_score_decode_lds(
+    const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ ctx_len,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q_idx,
+    const bf16* __restrict__ kidx, int Hkv, float* __restrict__ scores) {
+  constexpr int KW = DI / 32;
+  constexpr int GPW = 256 / DI;           // KV heads per wave at most (Hkv * DI <= 1024)
+  constexpr int LPT = kStageBytes / 16 / 256;  // 16-byte loads per thread per slice (8)
+  __shared__ __attribute__((aligned(16))) unsigned char stage[2][kStageLdsBytes];
+  const int b = blockIdx.x, r = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, qd = lane >> 4;
+  const int q0 = cu_q[r], nq = cu_q[r + 1] - q0, L = ctx_len[r];
+  const int RB = Hkv * DI * 2;            // bytes per token row (all KV heads)
+  const int RBP = RB + 16;                // padded LDS row
+  const int slice_bytes = 16 * RB;
+
+  for (int qc = 0; qc < nq; qc += 16) {
+    const int nqc = min(16, nq - qc);
+    const bool qvalid = n < nqc;
+    const int my_t = q0 + qc + (qvalid ? n : 0);
+    const int pos = qvalid ? q_pos[my_t] : -1;
+    const uint32_t qmask = qvalid ? 0xffffffffu : 0u;
+    int maxpos = pos;
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) maxpos = max(maxpos, __shfl_xor(maxpos, m, kWave));
+    if (b * kBlock > maxpos) {
+      for (int e = tid; e < nqc * Hkv; e += 256) {
+        const int t = q0 + qc + e / Hkv, g = e % Hkv;
+        scores[((int64_t)t * Hkv + g) * max_blocks + b] = neg_inf();
+      }
+      continue;
+    }
+    // slices holding at least one token that some query of the chunk may use
+    const int last_tok = min(min(maxpos, L - 1) - b * kBlock, kBlock - 1);
+    const int nsl = last_tok / 16 + 1;
+    const int page = block_table[(int64_t)r * max_blocks + b];
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(kidx) + (int64_t)page * kBlock * RB;
+
+    u32x4 qf[GPW][KW];
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      const int g = w + 4 * gi;
+#pragma unroll
+      for (int kw = 0; kw < KW; ++kw)
+        qf[gi][kw] = g < Hkv ? ld16(q_idx + ((int64_t)my_t * Hkv + g) * DI + 32 * kw + 8 * qd) & qmask : zero4();
+    }
+    float mx[GPW];
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) mx[gi] = neg_inf();
+
+    auto load_slice = [&](u32x4 (&reg)[LPT], int sl) {
+#pragma unroll
+      for (int u = 0; u < LPT; ++u) {
+        const int off = 16 * (tid + 256 * u);
+        reg[u] = off < slice_bytes ? ld16_nt(src + (int64_t)sl * slice_bytes + off) : zero4();
+      }
+    };
+    auto store_slice = [&](const u32x4 (&reg)[LPT], int buf) {
+#pragma unroll
+      for (int u = 0; u < LPT; ++u) {
+        const int off = 16 * (tid + 256 * u);
+        if (off < slice_bytes) st16(&stage[buf][(off / RB) * RBP + off % RB], reg[u]);
+      }
+    };
+    u32x4 regs[kStagePF][LPT];
+    load_slice(regs[0], 0);
+    if (nsl > 1) load_slice(regs[1], 1);
+    store_slice(regs[0], 0);
+    if (nsl > 2) load_slice(regs[0], 2);
+    __syncthreads();
+
+    // slice sl is in stage[sl & 1]; the registers regs[(sl + 1) & 1] hold slice sl + 1
+    auto step = [&](int sl, int buf, u32x4 (&reg)[LPT]) {
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) {
+        const int g = w + 4 * gi;
+        if (g < Hkv) {
+          f32x4 acc = fzero4();
+#pragma unroll
+          for (int kw = 0; kw < KW; ++kw) {
+            const u32x4 a = ld16(&stage[buf][n * RBP + g * DI * 2 + 64 * kw + 16 * qd]);
+            acc = mfma_bf16(a, qf[gi][kw], acc);
+          }
+          const int s0 = b * kBlock + 16 * sl + 4 * qd;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx[gi] = (s0 + i <= pos && s0 + i < L) ? fmaxf(mx[gi], acc[i]) : mx[gi];
+        }
+      }
+      __syncthreads();  // stage[buf ^ 1] (slice sl - 1) is no longer read
+      if (sl + 1 < nsl) {
+        store_slice(reg, buf ^ 1);
+        if (sl + 3 < nsl) load_slice(reg, sl + 3);
+      }
+      __syncthreads();
+    };
+    for (int sl = 0; sl < nsl; sl += 2) {
+      step(sl, 0, regs[1]);
+      if (sl + 1 < nsl) step(sl + 1, 1, regs[0]);
+    }
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      const int g = w + 4 * gi;
+      const float m = max_over_quads(mx[gi]);
+      if (g < Hkv && qd == 0 && qvalid) scores[((int64_t)(q0 + qc + n) * Hkv + g) * max_blocks + b] = m;
+    }
+  }
+}
+
 constexpr int kPrefTQ = 256;  // query rows per workgroup (64 per wave)
 constexpr int kPrefSB = 16;   // blocks buffered per score flush
 
@@ -239,6 +358,15 @@ hipError_t launch_score_decode(int B, int Di, const int32_t* block_table, int ma
   dim3 grid(max_blocks, B), block(256);
   const bf16* qi = static_cast<const bf16*>(q_idx);
   const bf16* ki = static_cast<const bf16*>(kidx);
+  if (Hkv * Di <= 1024) {
+    if (Di == 128)
+      hipLaunchKernelGGL(k_score_decode_lds<128>, grid, block, 0, stream, block_table, max_blocks, ctx_len, cu_q,
+                         q_pos, qi, ki, Hkv, scores);
+    else
+      hipLaunchKernelGGL(k_score_decode_lds<64>, grid, block, 0, stream, block_table, max_blocks, ctx_len, cu_q,
+                         q_pos, qi, ki, Hkv, scores);
+    return hipGetLastError();
+  }
   if (Di == 128)
     hipLaunchKernelGGL(k_score_decode<128>, grid, block, 0, stream, block_table, max_blocks, ctx_len, cu_q, q_pos,
                        qi, ki, Hkv, scores);

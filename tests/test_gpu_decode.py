@@ -25,6 +25,8 @@ CASES = {
     "k_exceeds_candidates": dict(ctx=[500, 200, 129], nq=[1, 1, 1], Hq=8, Hkv=2, D=128, Di=64, k=16),
     "g16_d64_di128": dict(ctx=[3000, 1500], nq=[2, 1], Hq=32, Hkv=2, D=64, Di=128, k=5),
     "g1_d128": dict(ctx=[1800, 900], nq=[1, 1], Hq=4, Hkv=4, D=128, Di=128, k=3),
+    # Hkv * Di > 1024: the decode scorer's direct-to-register variant
+    "hkv16_direct_scorer": dict(ctx=[900, 400], nq=[1, 2], Hq=32, Hkv=16, D=64, Di=128, k=3),
 }
 
 
