@@ -11,26 +11,31 @@
 
 namespace msa {
 
-__global__ __launch_bounds__(64) void k_topk(int B, int Hkv, int max_blocks, const int32_t* __restrict__ cu_q,
-                                             const int32_t* __restrict__ q_pos, const float* __restrict__ scores,
-                                             int k, int32_t* __restrict__ sel, int32_t* __restrict__ cnt) {
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void k_topk(int B, int Hkv, int max_blocks, const int32_t* __restrict__ cu_q,
+                                                  const int32_t* __restrict__ q_pos, const float* __restrict__ scores,
+                                                  int k, int32_t* __restrict__ sel, int32_t* __restrict__ cnt) {
+  constexpr int NT = 64 * NW;
   __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_red[2][NW];
+  __shared__ uint32_t s_cnt[2][NW];
+  __shared__ int s_bc[3];
   const int row = blockIdx.x;  // t*Hkv + g
   const int t = row / Hkv;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = min(q_pos[t] / kBlock + 1, max_blocks);
   const float* s = scores + (int64_t)row * max_blocks;
   int32_t* out = sel + (int64_t)row * k;
 
   if (n <= k) {
-    for (int i = lane; i < k; i += kWave) out[i] = i < n ? i : -1;
-    if (lane == 0) cnt[row] = n;
+    for (int i = tid; i < k; i += NT) out[i] = i < n ? i : -1;
+    if (tid == 0) cnt[row] = n;
     return;
   }
 
   // bits shared by every candidate key need no pass
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for (int i = lane; i < n; i += kWave) {
+  for (int i = tid; i < n; i += NT) {
     const uint32_t key = order_key(s[i]);
     kmin = min(kmin, key);
     kmax = max(kmax, key);
@@ -39,6 +44,11 @@ __global__ __launch_bounds__(64) void k_topk(int B, int Hkv, int max_blocks, con
   for (int m = 1; m < kWave; m <<= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, m, kWave));
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m, kWave));
+  }
+  if (NW > 1) {
+    if (lane == 0) { s_red[0][wv] = kmin; s_red[1][wv] = kmax; }
+    __syncthreads();
+    for (int x = 0; x < NW; ++x) { kmin = min(kmin, s_red[0][x]); kmax = max(kmax, s_red[1][x]); }
   }
   uint32_t prefix, mask;
   int remaining = k;
@@ -54,46 +64,43 @@ __global__ __launch_bounds__(64) void k_topk(int B, int Hkv, int max_blocks, con
       const int lo = max(top - 7, 0);
       const int width = top - lo + 1;
       const uint32_t dmask = ((1u << width) - 1u);
-      for (int i = lane; i < 256; i += kWave) hist[i] = 0u;
+      for (int i = tid; i < 256; i += NT) hist[i] = 0u;
       __syncthreads();
-      for (int i = lane; i < n; i += kWave) {
+      for (int i = tid; i < n; i += NT) {
         const uint32_t key = order_key(s[i]);
         if ((key & mask) == prefix) atomicAdd(&hist[(key >> lo) & dmask], 1u);
       }
       __syncthreads();
-      // lane l owns digits 255-4l .. 252-4l (descending); an inclusive scan over lanes gives
-      // the number of keys whose digit is at least a given value
-      uint32_t c[4], local = 0;
+      if (wv == 0) {
+        // lane l owns digits 255-4l .. 252-4l (descending); an inclusive scan over lanes gives
+        // the number of keys whose digit is at least a given value
+        uint32_t c[4], local = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; local += c[j]; }
-      uint32_t incl = local;
+        for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; local += c[j]; }
+        uint32_t incl = local;
 #pragma unroll
-      for (int m = 1; m < kWave; m <<= 1) {
-        const uint32_t o = (uint32_t)__shfl_up((int)incl, m, kWave);
-        if (lane >= m) incl += o;
-      }
-      uint32_t before = incl - local;
-      int found = -1;
-      uint32_t found_before = 0, found_cnt = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (found < 0 && before < (uint32_t)remaining && before + c[j] >= (uint32_t)remaining) {
-          found = 255 - 4 * lane - j;
-          found_before = before;
-          found_cnt = c[j];
+        for (int m = 1; m < kWave; m <<= 1) {
+          const uint32_t o = (uint32_t)__shfl_up((int)incl, m, kWave);
+          if (lane >= m) incl += o;
         }
-        before += c[j];
+        uint32_t before = incl - local;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (before < (uint32_t)remaining && before + c[j] >= (uint32_t)remaining) {
+            s_bc[0] = 255 - 4 * lane - j;   // exactly one lane and digit cross the boundary
+            s_bc[1] = (int)before;
+            s_bc[2] = (int)c[j];
+          }
+          before += c[j];
+        }
       }
-      const uint64_t hit = __ballot(found >= 0);
-      const int src = __ffsll((unsigned long long)hit) - 1;
-      const int digit = __shfl(found, src, kWave);
-      const uint32_t gt = (uint32_t)__shfl((int)found_before, src, kWave);
-      const uint32_t eq = (uint32_t)__shfl((int)found_cnt, src, kWave);
-      remaining -= (int)gt;
+      __syncthreads();
+      const int digit = s_bc[0], gt = s_bc[1], eq = s_bc[2];
+      remaining -= gt;
       prefix |= ((uint32_t)digit) << lo;
       mask |= dmask << lo;
       __syncthreads();
-      if (eq == (uint32_t)remaining) break;  // the whole boundary bucket is taken
+      if (eq == remaining) break;  // the whole boundary bucket is taken
       top = lo - 1;
     }
   }
@@ -101,23 +108,44 @@ __global__ __launch_bounds__(64) void k_topk(int B, int Hkv, int max_blocks, con
   // emit in id order: keys above the boundary, then the first `remaining` boundary ties
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int written = 0, ties_seen = 0;
-  for (int base = 0; base < n; base += kWave) {
-    const int i = base + lane;
+  for (int base = 0; base < n; base += NT) {
+    const int i = base + tid;
     const uint32_t hk = (i < n) ? (order_key(s[i]) & mask) : 0u;
     const bool gt = i < n && hk > prefix;
     const bool eq = i < n && hk == prefix;
     const uint64_t eqm = __ballot(eq);
-    const int eq_rank = ties_seen + __popcll(eqm & lt_mask);
-    const bool take = gt || (eq && eq_rank < remaining);
+    int eq_before = ties_seen + __popcll(eqm & lt_mask);
+    int eq_all = __popcll(eqm);
+    if (NW > 1) {
+      if (lane == 0) s_cnt[0][wv] = eq_all;
+      __syncthreads();
+      eq_all = 0;
+      for (int x = 0; x < NW; ++x) {
+        if (x < wv) eq_before += s_cnt[0][x];
+        eq_all += s_cnt[0][x];
+      }
+    }
+    const bool take = gt || (eq && eq_before < remaining);
     const uint64_t tm = __ballot(take);
-    const int slot = written + __popcll(tm & lt_mask);
+    int slot = written + __popcll(tm & lt_mask);
+    int take_all = __popcll(tm);
+    if (NW > 1) {
+      if (lane == 0) s_cnt[1][wv] = take_all;
+      __syncthreads();
+      take_all = 0;
+      for (int x = 0; x < NW; ++x) {
+        if (x < wv) slot += s_cnt[1][x];
+        take_all += s_cnt[1][x];
+      }
+      __syncthreads();  // s_cnt is rewritten by the next chunk
+    }
     if (take && slot < k) out[slot] = i;
-    written += __popcll(tm);
-    ties_seen += __popcll(eqm);
+    written += take_all;
+    ties_seen += eq_all;
   }
   written = min(written, k);
-  for (int i = written + lane; i < k; i += kWave) out[i] = -1;
-  if (lane == 0) cnt[row] = written;
+  for (int i = written + tid; i < k; i += NT) out[i] = -1;
+  if (tid == 0) cnt[row] = written;
 }
 
 // Decode sparse page table over the strided view (Chinese page, section "MSA需要新的分页注意力集成"):
@@ -151,8 +179,18 @@ __global__ __launch_bounds__(256) void k_page_table(int rows, int B, int Hkv, in
 
 hipError_t launch_topk(int B, int Nq, int Hkv, int max_blocks, const int32_t* cu_q, const int32_t* q_pos,
                        const float* scores, int k, int32_t* sel, int32_t* cnt, hipStream_t stream) {
-  hipLaunchKernelGGL(k_topk, dim3(Nq * Hkv), dim3(64), 0, stream, B, Hkv, max_blocks, cu_q, q_pos, scores, k, sel,
-                     cnt);
+  // few long rows: a workgroup of up to 16 waves per row; many rows: one wave each
+  const int rows = Nq * Hkv;
+  const int want = rows >= 4096 ? 1 : (max_blocks >= 4096 ? 16 : (max_blocks >= 1024 ? 4 : 1));
+  if (want == 16)
+    hipLaunchKernelGGL(k_topk<16>, dim3(rows), dim3(1024), 0, stream, B, Hkv, max_blocks, cu_q, q_pos, scores, k,
+                       sel, cnt);
+  else if (want == 4)
+    hipLaunchKernelGGL(k_topk<4>, dim3(rows), dim3(256), 0, stream, B, Hkv, max_blocks, cu_q, q_pos, scores, k, sel,
+                       cnt);
+  else
+    hipLaunchKernelGGL(k_topk<1>, dim3(rows), dim3(64), 0, stream, B, Hkv, max_blocks, cu_q, q_pos, scores, k, sel,
+                       cnt);
   return hipGetLastError();
 }
 

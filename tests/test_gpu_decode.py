@@ -27,6 +27,9 @@ CASES = {
     "g1_d128": dict(ctx=[1800, 900], nq=[1, 1], Hq=4, Hkv=4, D=128, Di=128, k=3),
     # Hkv * Di > 1024: the decode scorer's direct-to-register variant
     "hkv16_direct_scorer": dict(ctx=[900, 400], nq=[1, 2], Hq=32, Hkv=16, D=64, Di=128, k=3),
+    # few long rows: top-k runs 16 (>= 4096 blocks) and 4 (>= 1024 blocks) waves per row
+    "topk_16_waves": dict(ctx=[524300, 300001], nq=[1, 1], Hq=4, Hkv=1, D=64, Di=64, k=20),
+    "topk_4_waves": dict(ctx=[190000, 140000], nq=[1, 1], Hq=8, Hkv=2, D=64, Di=64, k=33),
 }
 
 
