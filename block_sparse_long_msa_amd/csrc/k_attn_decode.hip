@@ -149,6 +149,8 @@ __global__ __launch_bounds__(256) void k_lse_merge(int64_t rows, int parts, int 
                                                    bf16* __restrict__ out, float* __restrict__ lse_out) {
   __shared__ float s_w[4][kMergeMaxPG];
   __shared__ float s_lse[4][16];
+  __shared__ int s_parts[4][64];
+  __shared__ int s_np[4];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * 4 + wv;
   if (row >= rows) return;
@@ -175,26 +177,40 @@ __global__ __launch_bounds__(256) void k_lse_merge(int64_t rows, int parts, int 
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  // compact list of the parts present for at least one head (lane j tests part j; parts <= 64)
+  bool present = false;
+  if (lane < parts)
+    for (int h = 0; h < G; ++h) present = present || (pl[lane * G + h] != neg_inf());
+  const uint64_t pm = __ballot(present);
+  if (present) s_parts[wv][__popcll(pm & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))))] = lane;
+  const int np = __popcll(pm);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  const int* plist = s_parts[wv];
   for (int c = lane; c < GD / 8; c += kWave) {
     const int h = (8 * c) / D;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const TIn* src = part_o + (row * parts) * (int64_t)GD + 8 * c;
-#pragma unroll 8
-    for (int j = 0; j < parts; ++j) {
+#pragma unroll 4
+    for (int q = 0; q < np; ++q) {
+      const int j = plist[q];
       const float wj = w[j * G + h];
-      if (wj == 0.f) continue;  // absent part: never read
+      const bool use = wj != 0.f;  // a part absent for this head only: its values are never used
       if constexpr (sizeof(TIn) == 2) {
         const u32x4 v = ld16(src + (int64_t)j * GD);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += wj * __uint_as_float(v[e] << 16);
-          acc[2 * e + 1] += wj * __uint_as_float(v[e] & 0xffff0000u);
+          acc[2 * e] += use ? wj * __uint_as_float(v[e] << 16) : 0.f;
+          acc[2 * e + 1] += use ? wj * __uint_as_float(v[e] & 0xffff0000u) : 0.f;
         }
       } else {
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(src + (int64_t)j * GD);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + (int64_t)j * GD + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { acc[e] += wj * v0[e]; acc[4 + e] += wj * v1[e]; }
+        for (int e = 0; e < 4; ++e) {
+          acc[e] += use ? wj * v0[e] : 0.f;
+          acc[4 + e] += use ? wj * v1[e] : 0.f;
+        }
       }
     }
     u32x4 o;

@@ -14,6 +14,8 @@
 //    range, staging each key-index block in LDS once for 256 queries whose index vectors
 //    stay in registers, with the per-block max fused into the epilogue so that token-level
 //    scores never reach memory.
+#include <type_traits>
+
 #include "msa_device.h"
 
 #ifndef MSA_SCORE_PREFETCH
@@ -242,7 +244,7 @@ constexpr int kPrefTQ = 256;  // query rows per workgroup (64 per wave)
 constexpr int kPrefSB = 16;   // blocks buffered per score flush
 
 template <int DI>
-__global__ __launch_bounds__(256) void k_score_prefill(
+__global__ __launch_bounds__(256, 2) void k_score_prefill(
     int B, int Nq, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ ctx_len,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q_idx,
     const bf16* __restrict__ kidx, int Hkv, float* __restrict__ scores) {
@@ -287,17 +289,21 @@ __global__ __launch_bounds__(256) void k_score_prefill(
     pmin = min(min(wred[1][0], wred[1][1]), min(wred[1][2], wred[1][3]));
     const int nb = pmax / kBlock + 1;  // blocks needed by at least one row
 
+    // key-index block b+1 is loaded into registers while block b is multiplied from LDS
+    u32x4 stage[DI / 16];
+    auto load_block = [&](int bb) {
+      const int page = block_table[(int64_t)r * max_blocks + bb];
+      const bf16* kb = kidx + ((int64_t)page * kBlock * Hkv + g) * DI;
+#pragma unroll
+      for (int c = 0; c < DI / 16; ++c) {
+        const int idx = tid + 256 * c, tok = idx / (DI / 8), ch = idx % (DI / 8);
+        stage[c] = ld16(kb + (int64_t)tok * Hkv * DI + ch * 8);
+      }
+    };
+    load_block(0);
     for (int b0 = 0; b0 < nb; b0 += kPrefSB) {
       const int b1 = min(b0 + kPrefSB, nb);
       for (int b = b0; b < b1; ++b) {
-        const int page = block_table[(int64_t)r * max_blocks + b];
-        const bf16* kb = kidx + ((int64_t)page * kBlock * Hkv + g) * DI;
-        u32x4 stage[DI / 16];
-#pragma unroll
-        for (int c = 0; c < DI / 16; ++c) {
-          const int idx = tid + 256 * c, tok = idx / (DI / 8), ch = idx % (DI / 8);
-          stage[c] = ld16(kb + (int64_t)tok * Hkv * DI + ch * 8);
-        }
         __syncthreads();  // previous block fully consumed
 #pragma unroll
         for (int c = 0; c < DI / 16; ++c) {
@@ -305,30 +311,46 @@ __global__ __launch_bounds__(256) void k_score_prefill(
           st16(&ks[tok * KPAD + ch * 8], stage[c]);
         }
         __syncthreads();
+        if (b + 1 < nb) load_block(b + 1);
 
+        // full blocks (every key valid for every row) take the unmasked body; the branch is uniform
         const bool full = (b * kBlock + kBlock - 1 <= pmin) && (b * kBlock + kBlock - 1 < L);
         float mx[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
-#pragma unroll 2
-        for (int mt = 0; mt < 8; ++mt) {
-          u32x4 a[KW];
+        auto block_body = [&](auto masked) {
+          constexpr bool MASKED = decltype(masked)::value;
+          u32x4 a_cur[KW];
 #pragma unroll
-          for (int kw = 0; kw < KW; ++kw) a[kw] = ld16(&ks[(16 * mt + n) * KPAD + 32 * kw + 8 * qd]);
+          for (int kw = 0; kw < KW; ++kw) a_cur[kw] = ld16(&ks[n * KPAD + 32 * kw + 8 * qd]);
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            f32x4 acc = fzero4();
+          for (int mt = 0; mt < 8; ++mt) {
+            u32x4 a_nxt[KW];  // next 16-token tile's operands, read while this one multiplies
+            if (mt < 7) {
 #pragma unroll
-            for (int kw = 0; kw < KW; ++kw) acc = mfma_bf16(a[kw], qf[nt][kw], acc);
-            if (full) {
-              mx[nt] = fmaxf(mx[nt], fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
-            } else {
+              for (int kw = 0; kw < KW; ++kw) a_nxt[kw] = ld16(&ks[(16 * (mt + 1) + n) * KPAD + 32 * kw + 8 * qd]);
+            }
 #pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int s = b * kBlock + 16 * mt + 4 * qd + i;
-                if (s <= pos[nt] && s < L) mx[nt] = fmaxf(mx[nt], acc[i]);
+            for (int nt = 0; nt < 4; ++nt) {
+              f32x4 acc = fzero4();
+#pragma unroll
+              for (int kw = 0; kw < KW; ++kw) acc = mfma_bf16(a_cur[kw], qf[nt][kw], acc);
+              if constexpr (!MASKED) {
+                mx[nt] = fmaxf(fmaxf(mx[nt], fmaxf(acc[0], acc[1])), fmaxf(acc[2], acc[3]));
+              } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int s = b * kBlock + 16 * mt + 4 * qd + i;
+                  mx[nt] = (s <= pos[nt] && s < L) ? fmaxf(mx[nt], acc[i]) : mx[nt];
+                }
               }
             }
+            if (mt < 7) {
+#pragma unroll
+              for (int kw = 0; kw < KW; ++kw) a_cur[kw] = a_nxt[kw];
+            }
           }
-        }
+        };
+        if (full) block_body(std::false_type{});
+        else block_body(std::true_type{});
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
           const float v = max_over_quads(mx[nt]);
