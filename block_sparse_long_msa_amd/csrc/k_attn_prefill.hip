@@ -29,7 +29,7 @@
 
 namespace msa {
 
-constexpr int kChunk = 128;  // query tokens per work item
+constexpr int kChunk = 256;  // query tokens per work item
 constexpr int kNT = 2;       // 16-row MFMA N tiles per wave per pass
 constexpr int kXcds = 8;     // MI355X: workgroups are dealt round-robin to 8 XCDs
 constexpr float kLog2eP = 1.4426950408889634f;
