@@ -55,6 +55,23 @@ def make_workload(name, batch):
 
 # --- algorithmic work per launch ----------------------------------------------------------
 
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled against a plain copy), or None when there is none for this
+    workload or the kernel's source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(workload)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["traffic_bytes"]
+
+
 def candidate_tokens(wl):
     """Sum over (query row) of its candidate tokens: tokens 0 .. pos (all valid, pos < L)."""
     total = 0
@@ -223,7 +240,7 @@ def main():
     if decode:
         score_bytes = cand * wl.Hkv * wl.Di * 2                  # every candidate token's k_idx row, once
         roof = {"kernel": "k_score_decode", "bound": "hbm", "achieved": score_bytes / (score_ms * 1e-3) / 1e9,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": recorded_traffic(wl.name),
                 "algorithmic_bytes": score_bytes, "avg_ms": score_ms}
         attn_bytes = sel_tok * wl.D * 2 * 2                      # K and V rows of the selected tokens
         roof_attn = {"kernel": "k_attn_decode+k_lse_merge", "bound": "hbm",
