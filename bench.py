@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--no-flush", action="store_true", help="do not read 1 GiB between steps")
     p.add_argument("--cpu-budget-s", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--fused-topk", action="store_true",
+                   help="prefill: score and select with the fused msa_index_topk instead of two calls")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, run one plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -177,7 +179,10 @@ def main():
     gen_s = time.time() - t0
     b = msa.Batch(dev.block_table, dev.ctx_len, dev.cu_q, dev.q_pos, max(wl.q_counts))
     P = dev.kcache.shape[0]
-    run = (MSADecode if decode else MSAPrefill)(b, wl.Hkv, wl.G, wl.D, wl.k, P)
+    if decode:
+        run = MSADecode(b, wl.Hkv, wl.G, wl.D, wl.k, P)
+    else:
+        run = MSAPrefill(b, wl.Hkv, wl.G, wl.D, wl.k, P, fused=args.fused_topk)
     flush = None
     if not args.no_flush:
         flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -248,7 +253,7 @@ def main():
                      "algorithmic_bytes": attn_bytes, "avg_ms": attend_ms}
     else:
         score_flops = 2.0 * cand * wl.Hkv * wl.Di
-        roof = {"kernel": "k_score_prefill", "bound": "mfma",
+        roof = {"kernel": "k_score_prefill" + (" with fused top-k" if args.fused_topk else ""), "bound": "mfma",
                 "achieved": score_flops / (score_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "traffic": None, "algorithmic_flops": score_flops, "avg_ms": score_ms}
         attn_flops = 4.0 * sel_tok * wl.G * wl.D               # QK^T and PV over the selected tokens
@@ -269,7 +274,8 @@ def main():
         "config": {"workload": wl.name, "phase": "decode" if decode else "prefill", "requests": wl.B,
                    "query_tokens": wl.Nq, "ctx_len": wl.ctx_lens[0] if len(set(wl.ctx_lens)) == 1 else "ragged",
                    "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "Di": wl.Di, "top_k": wl.k, "block": wl.block,
-                   "l2_flush_between_steps": flush is not None},
+                   "l2_flush_between_steps": flush is not None,
+                   "fused_index_topk": bool(args.fused_topk and not decode)},
         "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
         "roofline_detail": [roof, roof_attn],
         "stage_ms": {name: float(per_stage[:, i].mean()) for i, name in enumerate(stages)},

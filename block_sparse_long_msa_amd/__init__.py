@@ -13,7 +13,8 @@ import torch
 
 from ._lib import EXPORTS, MsaBatch, MsaCache, MSAError, check, load  # noqa: F401
 
-__all__ = ["Batch", "MSAError", "msa_index_score", "msa_topk_blocks", "msa_build_sparse_page_table",
+__all__ = ["Batch", "MSAError", "msa_index_score", "msa_index_topk", "msa_index_topk_workspace_size",
+           "msa_topk_blocks", "msa_build_sparse_page_table",
            "msa_sparse_attn_decode", "msa_sparse_attn_decode_workspace_size", "msa_sparse_attn_prefill",
            "msa_sparse_attn_prefill_workspace_size", "msa_lse_merge", "msa_version", "load"]
 
@@ -79,6 +80,18 @@ def msa_index_score(batch: Batch, q_idx, k_idx, scores, stream=None) -> None:
     check("msa_index_score", load().msa_index_score(batch.ref(), _ptr(q_idx, torch.bfloat16, "q_idx"),
                                                      _cache(k_idx, "k_idx"), _ptr(scores, torch.float32, "scores"),
                                                      _stream(stream)))
+
+
+def msa_index_topk_workspace_size(batch: Batch, num_kv_heads: int, k: int) -> int:
+    return int(load().msa_index_topk_workspace_size(batch.ref(), num_kv_heads, k))
+
+
+def msa_index_topk(batch: Batch, q_idx, k_idx, k: int, sel, cnt, workspace=None, stream=None) -> None:
+    ws = _ptr(workspace, torch.uint8, "workspace", True)
+    check("msa_index_topk", load().msa_index_topk(batch.ref(), _ptr(q_idx, torch.bfloat16, "q_idx"),
+                                                   _cache(k_idx, "k_idx"), k, _ptr(sel, torch.int32, "sel"),
+                                                   _ptr(cnt, torch.int32, "cnt"), ws,
+                                                   0 if workspace is None else workspace.numel(), _stream(stream)))
 
 
 def msa_topk_blocks(batch: Batch, num_kv_heads: int, scores, k: int, sel, cnt, stream=None) -> None:

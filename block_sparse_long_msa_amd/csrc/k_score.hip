@@ -242,16 +242,24 @@ __global__ __launch_bounds__(256, 2) void k_score_decode_lds(
 
 constexpr int kPrefTQ = 256;  // query rows per workgroup (64 per wave)
 constexpr int kPrefSB = 16;   // blocks buffered per score flush
+constexpr int kFusedTopK = 16;  // largest k the fused scorer + top-k keeps per row
 
-template <int DI>
+// TOPK == 0: write the block scores.  TOPK > 0: fused top-k (k <= TOPK, block ids < 65536).  After
+// the cross-lane max every lane holds all four of its wave's row maxima, so lane (n, qd) adopts row
+// 16*qd + n of its wave and keeps that row's best k (score, block) pairs in its own registers.  Blocks
+// arrive in ascending id, so a new block enters only if it beats the current worst entry strictly
+// (equal scores keep the lower id), and the worst entry -- lowest score, highest id among equals --
+// is the one evicted.  The result equals msa_topk_blocks applied to the written scores.
+template <int DI, int TOPK>
 __global__ __launch_bounds__(256, 2) void k_score_prefill(
     int B, int Nq, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ ctx_len,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q_idx,
-    const bf16* __restrict__ kidx, int Hkv, float* __restrict__ scores) {
+    const bf16* __restrict__ kidx, int Hkv, float* __restrict__ scores, int k, int32_t* __restrict__ sel,
+    int32_t* __restrict__ cnt) {
   constexpr int KW = DI / 32;
   constexpr int KPAD = DI + 8;  // LDS row stride (elements): 16-lane ds_read_b128 groups hit 64 distinct banks
   __shared__ __attribute__((aligned(16))) bf16 ks[kBlock * KPAD];
-  __shared__ float sbuf[kPrefTQ][kPrefSB + 1];
+  __shared__ float sbuf[TOPK == 0 ? kPrefTQ : 1][kPrefSB + 1];
   __shared__ int wred[2][4];
 
   const int g = blockIdx.x % Hkv;  // consecutive workgroups take consecutive KV heads
@@ -288,6 +296,47 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
     pmax = max(max(wred[0][0], wred[0][1]), max(wred[0][2], wred[0][3]));
     pmin = min(min(wred[1][0], wred[1][1]), min(wred[1][2], wred[1][3]));
     const int nb = pmax / kBlock + 1;  // blocks needed by at least one row
+
+    // fused top-k state of the row this lane adopts (TOPK > 0)
+    const int lr = 64 * w + 16 * qd + n;  // local row
+    int my_last = -1;                     // last candidate block of the adopted row
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      if (nt == qd && pos[nt] >= 0) my_last = pos[nt] / kBlock;
+    int n_in = 0, worst_slot = 0, worst_id = 0;
+    float worst = neg_inf();
+    // the kept entries live in registers: scores, and block ids packed two per 32-bit word
+    constexpr int TK = TOPK > 0 ? TOPK : 2;
+    float top_s[TK];
+    uint32_t top_i[TK / 2];
+#pragma unroll
+    for (int j = 0; j < TK; ++j) top_s[j] = __builtin_inff();
+#pragma unroll
+    for (int j = 0; j < TK / 2; ++j) top_i[j] = 0u;
+    auto id_of = [&](int j) -> int { return (int)((top_i[j >> 1] >> (16 * (j & 1))) & 0xffffu); };
+    auto put = [&](int slot, float v, int id) {
+#pragma unroll
+      for (int j = 0; j < TK; ++j) {
+        top_s[j] = j == slot ? v : top_s[j];
+        if (j == slot) {
+          const int sh = 16 * (j & 1);
+          top_i[j >> 1] = (top_i[j >> 1] & ~(0xffffu << sh)) | ((uint32_t)id << sh);
+        }
+      }
+    };
+    auto rescan = [&]() {  // worst entry: lowest score, highest block id among equal scores
+      worst = __builtin_inff();
+      worst_id = -1;
+#pragma unroll
+      for (int j = 0; j < TK; ++j) {
+        const float sj = top_s[j];
+        const int ij = id_of(j);
+        const bool worse = j < k && (sj < worst || (sj == worst && ij > worst_id));
+        worst = worse ? sj : worst;
+        worst_id = worse ? ij : worst_id;
+        worst_slot = worse ? j : worst_slot;
+      }
+    };
 
     // key-index block b+1 is loaded into registers while block b is multiplied from LDS
     u32x4 stage[DI / 16];
@@ -351,24 +400,67 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
         };
         if (full) block_body(std::false_type{});
         else block_body(std::true_type{});
+        if constexpr (TOPK == 0) {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const float v = max_over_quads(mx[nt]);
-          if (qd == 0) sbuf[64 * w + 16 * nt + n][b - b0] = v;
+          for (int nt = 0; nt < 4; ++nt) {
+            const float v = max_over_quads(mx[nt]);
+            if (qd == 0) sbuf[64 * w + 16 * nt + n][b - b0] = v;
+          }
+        } else {
+          float mine = neg_inf();
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            const float v = max_over_quads(mx[nt]);
+            mine = nt == qd ? v : mine;
+          }
+          if (b <= my_last) {
+            if (n_in < k) {
+              put(n_in, mine, b);
+              if (++n_in == k) rescan();
+            } else if (mine > worst) {
+              put(worst_slot, mine, b);
+              rescan();
+            }
+          }
         }
       }
-      __syncthreads();
-      // flush: 16 consecutive threads write 16 consecutive blocks of one row
-      for (int it = 0; it < kPrefTQ / 16; ++it) {
-        const int lrow = it * 16 + (tid >> 4), bb = tid & 15, row = row0 + lrow, b = b0 + bb;
-        if (row >= qa && row < qb && b < b1) scores[((int64_t)row * Hkv + g) * max_blocks + b] = sbuf[lrow][bb];
+      if constexpr (TOPK == 0) {
+        __syncthreads();
+        // flush: 16 consecutive threads write 16 consecutive blocks of one row
+        for (int it = 0; it < kPrefTQ / 16; ++it) {
+          const int lrow = it * 16 + (tid >> 4), bb = tid & 15, row = row0 + lrow, b = b0 + bb;
+          if (row >= qa && row < qb && b < b1) scores[((int64_t)row * Hkv + g) * max_blocks + b] = sbuf[lrow][bb];
+        }
       }
     }
-    // non-candidate tail
-    const int tail = max_blocks - nb;
-    for (int e = tid; e < (qb - qa) * tail; e += 256) {
-      const int row = qa + e / tail, b = nb + e % tail;
-      scores[((int64_t)row * Hkv + g) * max_blocks + b] = neg_inf();
+    if constexpr (TOPK == 0) {
+      // non-candidate tail
+      const int tail = max_blocks - nb;
+      for (int e = tid; e < (qb - qa) * tail; e += 256) {
+        const int row = qa + e / tail, b = nb + e % tail;
+        scores[((int64_t)row * Hkv + g) * max_blocks + b] = neg_inf();
+      }
+    } else {
+      const int row = row0 + lr;
+      if (row >= qa && row < qb) {
+        int ids[TOPK];
+#pragma unroll
+        for (int j = 0; j < TOPK; ++j) ids[j] = j < n_in ? id_of(j) : 0x7fffffff;
+#pragma unroll
+        for (int a = 0; a < TOPK; ++a)  // ascending block ids (odd-even transposition sort)
+#pragma unroll
+          for (int j = a & 1; j + 1 < TOPK; j += 2) {
+            const int lo = min(ids[j], ids[j + 1]), hi = max(ids[j], ids[j + 1]);
+            ids[j] = lo;
+            ids[j + 1] = hi;
+          }
+        int32_t* out = sel + ((int64_t)row * Hkv + g) * k;
+#pragma unroll
+        for (int j = 0; j < TOPK; ++j)
+          if (j < k) out[j] = j < n_in ? ids[j] : -1;
+        for (int j = TOPK; j < k; ++j) out[j] = -1;
+        cnt[(int64_t)row * Hkv + g] = n_in;
+      }
     }
     __syncthreads();
   }
@@ -406,11 +498,30 @@ hipError_t launch_score_prefill(int B, int Nq, int Di, const int32_t* block_tabl
   const bf16* qi = static_cast<const bf16*>(q_idx);
   const bf16* ki = static_cast<const bf16*>(kidx);
   if (Di == 128)
-    hipLaunchKernelGGL(k_score_prefill<128>, grid, block, 0, stream, B, Nq, block_table, max_blocks, ctx_len, cu_q,
-                       q_pos, qi, ki, Hkv, scores);
+    hipLaunchKernelGGL((k_score_prefill<128, 0>), grid, block, 0, stream, B, Nq, block_table, max_blocks, ctx_len,
+                       cu_q, q_pos, qi, ki, Hkv, scores, 0, nullptr, nullptr);
   else
-    hipLaunchKernelGGL(k_score_prefill<64>, grid, block, 0, stream, B, Nq, block_table, max_blocks, ctx_len, cu_q,
-                       q_pos, qi, ki, Hkv, scores);
+    hipLaunchKernelGGL((k_score_prefill<64, 0>), grid, block, 0, stream, B, Nq, block_table, max_blocks, ctx_len,
+                       cu_q, q_pos, qi, ki, Hkv, scores, 0, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+int fused_topk_capacity() { return kFusedTopK; }
+
+hipError_t launch_score_topk_prefill(int B, int Nq, int Di, const int32_t* block_table, int max_blocks,
+                                     const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos,
+                                     const void* q_idx, const void* kidx, int Hkv, int k, int32_t* sel, int32_t* cnt,
+                                     hipStream_t stream) {
+  const int tiles = (Nq + kPrefTQ - 1) / kPrefTQ;
+  dim3 grid(tiles * Hkv), block(256);
+  const bf16* qi = static_cast<const bf16*>(q_idx);
+  const bf16* ki = static_cast<const bf16*>(kidx);
+  if (Di == 128)
+    hipLaunchKernelGGL((k_score_prefill<128, kFusedTopK>), grid, block, 0, stream, B, Nq, block_table, max_blocks,
+                       ctx_len, cu_q, q_pos, qi, ki, Hkv, nullptr, k, sel, cnt);
+  else
+    hipLaunchKernelGGL((k_score_prefill<64, kFusedTopK>), grid, block, 0, stream, B, Nq, block_table, max_blocks,
+                       ctx_len, cu_q, q_pos, qi, ki, Hkv, nullptr, k, sel, cnt);
   return hipGetLastError();
 }
 

@@ -15,6 +15,11 @@ hipError_t launch_score_decode(int B, int Di, const int32_t* block_table, int ma
 hipError_t launch_score_prefill(int B, int Nq, int Di, const int32_t* block_table, int max_blocks,
                                 const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const void* q_idx,
                                 const void* kidx, int Hkv, float* scores, hipStream_t stream);
+int fused_topk_capacity();
+hipError_t launch_score_topk_prefill(int B, int Nq, int Di, const int32_t* block_table, int max_blocks,
+                                     const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos,
+                                     const void* q_idx, const void* kidx, int Hkv, int k, int32_t* sel, int32_t* cnt,
+                                     hipStream_t stream);
 hipError_t launch_topk(int B, int Nq, int Hkv, int max_blocks, const int32_t* cu_q, const int32_t* q_pos,
                        const float* scores, int k, int32_t* sel, int32_t* cnt, hipStream_t stream);
 hipError_t launch_page_table(int B, int Nq, int Hkv, int max_blocks, const int32_t* block_table,
@@ -136,6 +141,43 @@ msa_status msa_index_score(const msa_batch* batch, const void* q_idx, msa_cache 
                                   batch->max_blocks, batch->ctx_len, batch->cu_q, batch->q_pos, q_idx, k_idx.data,
                                   k_idx.num_heads, scores, st);
   return from_hip(e, "msa_index_score launch");
+}
+
+static bool fused_index_topk(const msa_batch* b, int32_t k) {
+  return b->max_q_per_request > 16 && k <= msa::fused_topk_capacity() && b->max_blocks <= 65536;
+}
+
+size_t msa_index_topk_workspace_size(const msa_batch* batch, int32_t num_kv_heads, int32_t k) {
+  if (!batch || batch->num_queries < 0 || batch->max_blocks <= 0 || num_kv_heads <= 0 || k <= 0) return 0;
+  if (fused_index_topk(batch, k)) return 0;
+  return align256((size_t)batch->num_queries * num_kv_heads * batch->max_blocks * sizeof(float));
+}
+
+msa_status msa_index_topk(const msa_batch* batch, const void* q_idx, msa_cache k_idx, int32_t k, int32_t* sel,
+                          int32_t* cnt, void* workspace, size_t workspace_bytes, msa_stream_t stream) {
+  g_last_error.clear();
+  if (msa_status s = check_batch(batch)) return s;
+  if (msa_status s = check_cache(k_idx, "k_idx")) return s;
+  MSA_REQUIRE(k >= 1 && k <= kMaxK, MSA_ERR_UNSUPPORTED, "k must be in [1, %d], got %d", kMaxK, k);
+  MSA_REQUIRE(batch->num_queries == 0 || (q_idx && aligned16(q_idx) && sel && cnt), MSA_ERR_INVALID_ARG,
+              "q_idx (16-byte aligned), sel and cnt must be non-NULL");
+  MSA_REQUIRE(aligned4(sel) && aligned4(cnt), MSA_ERR_INVALID_ARG, "sel and cnt must be 4-byte aligned");
+  MSA_REQUIRE((int64_t)batch->num_queries * k_idx.num_heads <= 0x7fffffff, MSA_ERR_UNSUPPORTED,
+              "num_queries * num_kv_heads exceeds the grid limit");
+  if (batch->num_queries == 0) return MSA_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (fused_index_topk(batch, k))
+    return from_hip(msa::launch_score_topk_prefill(batch->num_requests, batch->num_queries, k_idx.head_dim,
+                                                   batch->block_table, batch->max_blocks, batch->ctx_len,
+                                                   batch->cu_q, batch->q_pos, q_idx, k_idx.data, k_idx.num_heads, k,
+                                                   sel, cnt, st),
+                    "msa_index_topk launch");
+  const size_t need = msa_index_topk_workspace_size(batch, k_idx.num_heads, k);
+  MSA_REQUIRE(workspace && aligned16(workspace) && workspace_bytes >= need, MSA_ERR_WORKSPACE_TOO_SMALL,
+              "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+  float* scores = static_cast<float*>(workspace);
+  if (msa_status s = msa_index_score(batch, q_idx, k_idx, scores, stream)) return s;
+  return msa_topk_blocks(batch, k_idx.num_heads, scores, k, sel, cnt, stream);
 }
 
 msa_status msa_topk_blocks(const msa_batch* batch, int32_t num_kv_heads, const float* scores, int32_t k,

@@ -10,9 +10,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (Batch, msa_build_sparse_page_table, msa_index_score, msa_lse_merge, msa_sparse_attn_decode,
-               msa_sparse_attn_decode_workspace_size, msa_sparse_attn_prefill,
-               msa_sparse_attn_prefill_workspace_size, msa_topk_blocks)
+from . import (Batch, msa_build_sparse_page_table, msa_index_score, msa_index_topk, msa_index_topk_workspace_size,
+               msa_lse_merge, msa_sparse_attn_decode, msa_sparse_attn_decode_workspace_size,
+               msa_sparse_attn_prefill, msa_sparse_attn_prefill_workspace_size, msa_topk_blocks)
 
 
 class MSADecode:
@@ -50,10 +50,18 @@ class MSADecode:
 
 
 class MSAPrefill:
-    def __init__(self, batch: Batch, Hkv: int, G: int, D: int, k: int, num_pages: int, device="cuda"):
+    """``fused=True`` scores and selects in one call (msa_index_topk): block scores never reach memory
+    when the shape allows it, and ``scores`` is then not kept.  The two-call route is the default: on
+    the long-prefill workload it is still slightly faster."""
+
+    def __init__(self, batch: Batch, Hkv: int, G: int, D: int, k: int, num_pages: int, device="cuda",
+                 fused: bool = False):
         Nq, mb = batch.num_queries, batch.max_blocks
         self.batch, self.Hkv, self.G, self.D, self.k, self.num_pages = batch, Hkv, G, D, k, num_pages
-        self.scores = torch.empty((Nq, Hkv, mb), dtype=torch.float32, device=device)
+        self.fused = fused
+        self.scores = None if fused else torch.empty((Nq, Hkv, mb), dtype=torch.float32, device=device)
+        self.topk_ws = torch.empty((max(1, msa_index_topk_workspace_size(batch, Hkv, k)),), dtype=torch.uint8,
+                                   device=device)
         self.sel = torch.empty((Nq, Hkv, k), dtype=torch.int32, device=device)
         self.cnt = torch.empty((Nq, Hkv), dtype=torch.int32, device=device)
         self.part_o = torch.empty((Nq, Hkv, k, G, D), dtype=torch.bfloat16, device=device)
@@ -64,10 +72,14 @@ class MSAPrefill:
                               device=device)
 
     def score(self, q_idx, kidx, stream=None):
-        msa_index_score(self.batch, q_idx, kidx, self.scores, stream)
+        if self.fused:
+            msa_index_topk(self.batch, q_idx, kidx, self.k, self.sel, self.cnt, self.topk_ws, stream)
+        else:
+            msa_index_score(self.batch, q_idx, kidx, self.scores, stream)
 
     def select(self, stream=None):
-        msa_topk_blocks(self.batch, self.Hkv, self.scores, self.k, self.sel, self.cnt, stream)
+        if not self.fused:
+            msa_topk_blocks(self.batch, self.Hkv, self.scores, self.k, self.sel, self.cnt, stream)
 
     def attend(self, q, kcache, vcache, sm_scale: float, stream=None):
         msa_sparse_attn_prefill(self.batch, self.G, q, kcache, vcache, self.sel, self.cnt, self.k, sm_scale,

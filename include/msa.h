@@ -99,6 +99,19 @@ msa_status msa_index_score(const msa_batch* batch, const void* q_idx, msa_cache 
 msa_status msa_topk_blocks(const msa_batch* batch, int32_t num_kv_heads, const float* scores, int32_t k,
                            int32_t* sel, int32_t* cnt, msa_stream_t stream);
 
+/* Fused index scoring + top-k.  The pages name fusing MSA's small kernels (top-k over KV blocks,
+ * per-block scoring and reduction) as the open opportunity (Chinese page, section "遗留问题";
+ * Japanese page, "今後の取り組み").  The result is identical to msa_index_score followed by
+ * msa_topk_blocks -- same fp32 block scores, same tie rule -- but for prefill shapes
+ * (batch->max_q_per_request > 16) with k <= 16 the block scores never reach memory: the scoring
+ * kernel keeps every query row's running top-k on chip.  Other shapes run the two kernels through
+ * the workspace.
+ *   sel, cnt   as msa_topk_blocks
+ *   workspace  device, >= msa_index_topk_workspace_size(...) bytes (may be 0 / NULL) */
+msa_status msa_index_topk(const msa_batch* batch, const void* q_idx, msa_cache k_idx, int32_t k, int32_t* sel,
+                          int32_t* cnt, void* workspace, size_t workspace_bytes, msa_stream_t stream);
+size_t msa_index_topk_workspace_size(const msa_batch* batch, int32_t num_kv_heads, int32_t k);
+
 /* Sparse per-row page table for decode (Chinese page, section "MSA需要新的分页注意力集成"):
  * row rho = t*Hkv + g of the flattened (query row, KV head) batch gets
  *   page_table[rho, j] = block_table[r, sel[t,g,j]] * 128 * Hkv + g   (j < cnt[t,g]; -1 after)

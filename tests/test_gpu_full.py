@@ -115,12 +115,18 @@ def test_long_prefill_full():
     announce("full", wl.name)
     dev = mi.make_inputs(wl, "cuda")
     b = msa.Batch(dev.block_table, dev.ctx_len, dev.cu_q, dev.q_pos, max(wl.q_counts))
-    run = MSAPrefill(b, wl.Hkv, wl.G, wl.D, wl.k, dev.kcache.shape[0])
+    run = MSAPrefill(b, wl.Hkv, wl.G, wl.D, wl.k, dev.kcache.shape[0], fused=False)
     run.out.fill_(float("nan"))
     run(dev.q, dev.q_idx, dev.kcache, dev.vcache, dev.kidx, dev.scale)
     torch.cuda.synchronize()
     m = _host_meta(dev)
     s, sel, cnt = host(run.scores), host(run.sel), host(run.cnt)
+    # the fused scorer + top-k selects exactly the same blocks
+    fused = MSAPrefill(b, wl.Hkv, wl.G, wl.D, wl.k, dev.kcache.shape[0], fused=True)
+    fused(dev.q, dev.q_idx, dev.kcache, dev.vcache, dev.kidx, dev.scale)
+    assert np.array_equal(host(fused.sel), sel) and np.array_equal(host(fused.cnt), cnt)
+    assert np.array_equal(host(fused.out).view(np.uint32), host(run.out).view(np.uint32))
+    del fused
     # every row: exact top-k on the GPU's scores, counts, finite outputs, absent slots marked
     o_sel, o_cnt = oracle.topk_blocks(s.astype(np.float64), m["pos"], wl.block, wl.k)
     assert np.array_equal(sel, o_sel) and np.array_equal(cnt, o_cnt)
