@@ -75,7 +75,8 @@ def recorded_traffic(workload: str):
 
 
 def candidate_tokens(wl):
-    """Sum over (query row) of its candidate tokens: tokens 0 .. pos (all valid, pos < L)."""
+    """Sum over (query row) of its candidate tokens: tokens 0 .. pos (all valid, pos < L).
+    This counts multiply-adds: every query row scores every one of its candidate tokens."""
     total = 0
     for L, nq in zip(wl.ctx_lens, wl.q_counts):
         first = L - nq
@@ -83,15 +84,29 @@ def candidate_tokens(wl):
     return total
 
 
-def selected_tokens(dev, sel, cnt):
-    """Valid tokens over the selected blocks, summed over (query row, KV head)."""
+def candidate_tokens_union(wl):
+    """Tokens whose key-index rows some query row needs, each counted once per request (the queries of
+    one request share their candidate range): the bytes a decode scorer must read."""
+    return sum(L for L in wl.ctx_lens)
+
+
+def selected_tokens(dev, sel, cnt, union: bool = False):
+    """Valid tokens over the selected blocks, summed over (query row, KV head); with ``union``, each
+    (request, KV head, block) is counted once however many query rows of the request selected it."""
     BS = dev.wl.block
     req = dev.q_req.long()
     lim = torch.minimum(dev.q_pos.long() + 1, dev.ctx_len.long()[req])          # [Nq]
     s = sel.long()
     valid = torch.clamp(lim[:, None, None] - s * BS, min=0, max=BS)
     mask = torch.arange(sel.shape[2], device=sel.device)[None, None, :] < cnt[:, :, None]
-    return int((valid * mask).sum().item())
+    if not union:
+        return int((valid * mask).sum().item())
+    Nq, Hkv, k = sel.shape
+    mb = dev.block_table.shape[1]
+    key = (req[:, None, None] * Hkv + torch.arange(Hkv, device=sel.device)[None, :, None]) * mb + s.clamp(min=0)
+    best = torch.zeros(dev.wl.B * Hkv * mb, dtype=torch.long, device=sel.device)
+    best.scatter_reduce_(0, key[mask], valid[mask], reduce="amax")
+    return int(best.sum().item())
 
 
 # --- cpu_baseline: the CPU oracle, timed on a bounded sample of the same workload ---------------
@@ -241,9 +256,9 @@ def main():
     score_ms = float(per_stage[:, 0].mean())
     attend_ms = float(per_stage[:, 2].mean())
     cand = candidate_tokens(wl)
-    sel_tok = selected_tokens(dev, run.sel, run.cnt)
     if decode:
-        score_bytes = cand * wl.Hkv * wl.Di * 2                  # every candidate token's k_idx row, once
+        sel_tok = selected_tokens(dev, run.sel, run.cnt, union=True)
+        score_bytes = candidate_tokens_union(wl) * wl.Hkv * wl.Di * 2   # every needed k_idx row, once
         roof = {"kernel": "k_score_decode", "bound": "hbm", "achieved": score_bytes / (score_ms * 1e-3) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": recorded_traffic(wl.name),
                 "algorithmic_bytes": score_bytes, "avg_ms": score_ms}
@@ -252,6 +267,7 @@ def main():
                      "achieved": attn_bytes / (attend_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "algorithmic_bytes": attn_bytes, "avg_ms": attend_ms}
     else:
+        sel_tok = selected_tokens(dev, run.sel, run.cnt)
         score_flops = 2.0 * cand * wl.Hkv * wl.Di
         roof = {"kernel": "k_score_prefill" + (" with fused top-k" if args.fused_topk else ""), "bound": "mfma",
                 "achieved": score_flops / (score_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -96,6 +96,14 @@ def agentic_decode(seed: int = 1001, batch: int = 8) -> Workload:
                     k=16, hot_per_group=16, hot_ref="query", seed=seed)
 
 
+def spec_decode(seed: int = 1005, batch: int = 8, draft: int = 4) -> Workload:
+    """Multi-token decode (speculative verification): the agentic decode with `draft` query tokens per
+    request (the last `draft` tokens of a 61440 + `draft` context), each scoring, selecting and
+    attending on its own causal range; 16 hot blocks per (request, group)."""
+    return Workload(f"spec_decode_b{batch}_x{draft}_61k", ctx_lens=[61440 + draft] * batch, q_counts=[draft] * batch,
+                    k=16, hot_per_group=16, hot_ref="query", seed=seed)
+
+
 def long_prefill(seed: int = 1002, new_tokens: int = 32768, prefix: int = 98304) -> Workload:
     """32768 new tokens over a 98304-token cached prefix (131072 total, 1024 blocks), top-16,
     q_idx drawn from 64 per-group centroids plus N(0, 0.1^2) noise."""
@@ -135,6 +143,7 @@ WORKLOADS = {
     "long_prefill": long_prefill,
     "million_decode": million_decode,
     "ragged_decode": ragged_decode,
+    "spec_decode": spec_decode,
 }
 
 

@@ -96,6 +96,17 @@ def test_million_decode_full():
     _check_requests_decode(dev, run, m, [0], s, sel, cnt, out)     # all 8192 blocks of every KV head
 
 
+def test_spec_decode_full():
+    """Four query tokens per request share one pass of the scorer over each page."""
+    wl = mi.spec_decode()
+    announce("full", wl.name)
+    dev = mi.make_inputs(wl, "cuda")
+    run = _decode_run(dev)
+    m = _host_meta(dev)
+    s, sel, cnt, out = _check_all_rows_decode(dev, run, m)
+    _check_requests_decode(dev, run, m, [0, 7], s, sel, cnt, out)
+
+
 def test_ragged_decode_full():
     wl = mi.ragged_decode()
     announce("full", wl.name)
