@@ -14,7 +14,7 @@ import torch
 from ._lib import EXPORTS, MsaBatch, MsaCache, MSAError, check, load  # noqa: F401
 
 __all__ = ["Batch", "MSAError", "msa_index_score", "msa_index_topk", "msa_index_topk_workspace_size",
-           "msa_topk_blocks", "msa_build_sparse_page_table",
+           "msa_topk_blocks", "msa_build_sparse_page_table", "msa_topk_page_table",
            "msa_sparse_attn_decode", "msa_sparse_attn_decode_workspace_size", "msa_sparse_attn_prefill",
            "msa_sparse_attn_prefill_workspace_size", "msa_lse_merge", "msa_version", "load"]
 
@@ -107,6 +107,15 @@ def msa_build_sparse_page_table(batch: Batch, num_kv_heads: int, num_pages: int,
                                              _ptr(cnt, torch.int32, "cnt"), k,
                                              _ptr(page_table, torch.int32, "page_table"),
                                              _ptr(row_len, torch.int32, "row_len"), _stream(stream)))
+
+
+def msa_topk_page_table(batch: Batch, num_kv_heads: int, num_pages: int, scores, k: int, sel, cnt, page_table,
+                        row_len, stream=None) -> None:
+    check("msa_topk_page_table",
+          load().msa_topk_page_table(batch.ref(), num_kv_heads, num_pages, _ptr(scores, torch.float32, "scores"), k,
+                                     _ptr(sel, torch.int32, "sel"), _ptr(cnt, torch.int32, "cnt"),
+                                     _ptr(page_table, torch.int32, "page_table"),
+                                     _ptr(row_len, torch.int32, "row_len"), _stream(stream)))
 
 
 def msa_sparse_attn_decode_workspace_size(rows: int, G: int, D: int, k: int) -> int:

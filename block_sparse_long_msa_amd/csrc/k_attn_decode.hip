@@ -5,16 +5,20 @@
 // (virtual page v at v*page_stride, tokens every token_stride elements) -- Chinese page of
 // the MiniMax-M3 serving write-up, section "MSA需要新的分页注意力集成".
 //
-// k_attn_decode: one workgroup per (row, page); the four waves take 32 tokens each.
+// k_attn_decode: one workgroup per (row, run of pages); the four waves take 32 tokens of every
+//   page each and keep a running softmax over the run.
 //   S^T = K Q^T on bf16 MFMA with the tokens as M and the G query heads padded into N.
 //   P stays in the MFMA result registers and feeds O^T = V^T P^T directly as the B operand of
 //   an fp32 16x16x4 MFMA: lane (n, q) holds P for tokens 4q+i, and loads the matching V row
 //   as 16 contiguous bytes, whose 8 values become the A operand of 8 MFMAs (output row m of
 //   MFMA c is d = 8m + c).  No LDS transpose, no shuffles, every V row read as whole
-//   64-byte segments.  The four waves' (max, sum, O) are combined through LDS and written as
-//   one fp32 partial per (row, page).
+//   64-byte segments.  The four waves' (max, sum, O) are combined through LDS.  A row is split
+//   over several workgroups only as far as needed to occupy the chip; the splits are then
+//   combined by k_merge_splits.
 // k_lse_merge: LSE = log sum_j exp(lse_j); O = sum_j exp(lse_j - LSE) O_j over the parts with
 //   lse_j > -inf (section "KV块主序稀疏注意力减少冗余KV移动").
+#include <algorithm>
+
 #include "msa_device.h"
 
 namespace msa {
@@ -22,56 +26,57 @@ namespace msa {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+#ifndef MSA_DECODE_TARGET_WGS
+#define MSA_DECODE_TARGET_WGS 256  // workgroups a decode launch aims for (one per CU, two pages in flight each)
+#endif
+
+// One page's operands for one lane of wave w: K rows 32w + 16sub + n (16-byte chunk kw, qd of
+// each) and V rows 32w + 16sub + 4qd + i (elements 8n .. 8n+7).
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_decode(
-    int G, const bf16* __restrict__ q, const bf16* __restrict__ kview, const bf16* __restrict__ vview,
-    int64_t page_stride, int64_t token_stride, const int32_t* __restrict__ page_table, int k,
-    const int32_t* __restrict__ row_len, float scale_log2, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
-  constexpr int KW = D / 32;
-  __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ float sm_o[4][16][D];
-  const int j = blockIdx.x, rho = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, qd = lane >> 4;
-  const int len = row_len[rho];
-  const int npages = (len + kBlock - 1) / kBlock;
-  const int64_t part = (int64_t)rho * k + j;
-  if (j >= npages) {
-    if (tid < G) ws_lse[part * G + tid] = neg_inf();
-    return;
-  }
-  const int64_t vpage = page_table[part];
-  const bf16* kb = kview + vpage * page_stride;
-  const bf16* vb = vview + vpage * page_stride;
-  const int valid = min(kBlock, len - j * kBlock);
+struct PageRegs {
+  u32x4 k[2][D / 32];
+  u32x4 v[2][4];
+};
 
-  u32x4 qf[KW];
+// Issue every load of one page.  A token index past the row's end is clamped to the last valid
+// token, so every address stays inside the row and every loaded value is a finite cache entry;
+// such tokens get probability exactly 0 below.  The loads carry no condition, so all of them are
+// in flight together.  Each K load instruction covers half of every token's 128-byte line and
+// the next one the other half, so K goes through L1 (ordinary loads); V rows are read as whole
+// lines and stream past it (non-temporal).  (For D = 64 the lanes n >= 8 re-read chunk n - 8: same cache lines, and
+// the MFMA rows they feed, d >= 64, are never stored.)
+template <int D>
+__device__ __forceinline__ void load_page(PageRegs<D>& r, const bf16* kb, const bf16* vb, int ts, int valid,
+                                          int w, int n, int qd) {
 #pragma unroll
-  for (int kw = 0; kw < KW; ++kw)
-    qf[kw] = (n < G) ? ld16(q + ((int64_t)rho * G + n) * D + 32 * kw + 8 * qd) : zero4();
-
-  // V rows this lane needs: token 32w + 16sub + 4qd + i, elements 8n .. 8n+7
-  u32x4 vr[2][4];
+  for (int sub = 0; sub < 2; ++sub) {
+    const int tok = min(32 * w + 16 * sub + n, valid - 1);
+#pragma unroll
+    for (int kw = 0; kw < D / 32; ++kw) r.k[sub][kw] = ld16(kb + tok * ts + 32 * kw + 8 * qd);
+  }
+  const int dv = (8 * n) & (D - 1);
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tok = 32 * w + 16 * sub + 4 * qd + i;
-      vr[sub][i] = (tok < valid && 8 * n < D) ? ld16_nt(vb + (int64_t)tok * token_stride + 8 * n) : zero4();
+      const int tok = min(32 * w + 16 * sub + 4 * qd + i, valid - 1);
+      r.v[sub][i] = ld16_nt(vb + tok * ts + dv);
     }
+}
 
+// Fold one page into the wave's running (m, l, O) for head n (online softmax, base 2).
+template <int D>
+__device__ __forceinline__ void attend_page(const PageRegs<D>& r, const u32x4 (&qf)[D / 32], int valid, int w,
+                                            int qd, float scale_log2, float& m, float& l, f32x4 (&acc)[8]) {
   f32x4 s[2];
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
-    const int tok = 32 * w + 16 * sub + n;
     s[sub] = fzero4();
 #pragma unroll
-    for (int kw = 0; kw < KW; ++kw) {
-      const u32x4 a = (tok < valid) ? ld16_nt(kb + (int64_t)tok * token_stride + 32 * kw + 8 * qd) : zero4();
-      s[sub] = mfma_bf16(a, qf[kw], s[sub]);
-    }
+    for (int kw = 0; kw < D / 32; ++kw) s[sub] = mfma_bf16(r.k[sub][kw], qf[kw], s[sub]);
   }
   // s[sub][i] = S[token 32w + 16sub + 4qd + i][head n]
-  float m = neg_inf();
+  float mp = neg_inf();
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -79,28 +84,30 @@ __global__ __launch_bounds__(256) void k_attn_decode(
       const int tok = 32 * w + 16 * sub + 4 * qd + i;
       const float x = (tok < valid) ? s[sub][i] * scale_log2 : neg_inf();
       s[sub][i] = x;
-      m = fmaxf(m, x);
+      mp = fmaxf(mp, x);
     }
-  m = max_over_quads(m);
-  float l = 0.f;
+  const float mn = fmaxf(m, max_over_quads(mp));
+  const float alpha = (m == neg_inf()) ? 0.f : fast_exp2(m - mn);
+  m = mn;
+  float ls = 0.f;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float p = (m == neg_inf()) ? 0.f : fast_exp2(s[sub][i] - m);
+      const float p = (mn == neg_inf()) ? 0.f : fast_exp2(s[sub][i] - mn);
       s[sub][i] = p;
-      l += p;
+      ls += p;
     }
-  l = sum_over_quads(l);
-
-  f32x4 acc[8];
+  l = l * alpha + sum_over_quads(ls);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = fzero4();
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[c][e] *= alpha;
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const u32x4 v = vr[sub][i];
+      const u32x4 v = r.v[sub][i];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const uint32_t word = v[c >> 1];
@@ -108,33 +115,177 @@ __global__ __launch_bounds__(256) void k_attn_decode(
         acc[c] = mfma_f32(vf, s[sub][i], acc[c]);
       }
     }
-  // acc[c][ii] = O_w[head n][d = 32qd + 8ii + c]
+}
+
+// Workgroup (split s, row rho) attends to the row's pages [s*ppw, (s+1)*ppw) with two pages of
+// loads in flight (one being consumed, the next arriving).  With nsplit = 1 it writes the final
+// bf16 output and LSE; otherwise an fp32 partial and its LSE per (row, split) for the merge.
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_attn_decode(
+    int G, const bf16* __restrict__ q, const bf16* __restrict__ kview, const bf16* __restrict__ vview,
+    int64_t page_stride, int64_t token_stride, const int32_t* __restrict__ page_table, int k,
+    const int32_t* __restrict__ row_len, float scale_log2, int ppw, int nsplit, bf16* __restrict__ out,
+    float* __restrict__ lse_out, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+  constexpr int KW = D / 32;
+  constexpr int OST = D + 4;  // padded LDS row of the per-wave outputs
+  __shared__ float sm_m[4][16], sm_l[4][16];
+  __shared__ __align__(16) float sm_o[4][16][OST];
+  const int sp = blockIdx.x, rho = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, qd = lane >> 4;
+  const int j0 = sp * ppw;
+  const int32_t* pt = page_table + (int64_t)rho * k;
+  // the first two page ids are read together with the row length (both in bounds of the row's k
+  // entries), so the first K/V loads wait for one round trip, not two
+  const int pt0 = pt[j0], pt1 = pt[min(j0 + 1, k - 1)];
+  const int len = row_len[rho];
+  asm volatile("" ::"s"(pt0), "s"(pt1), "s"(len));  // issue the three loads here, side by side
+  const int npages = (len + kBlock - 1) / kBlock;
+  const int j1 = min(j0 + ppw, npages);
+  const int64_t part = (int64_t)rho * nsplit + sp;
+  if (j0 >= j1) {  // only with nsplit > 1: a split past the row's last page
+    if (tid < G) ws_lse[part * G + tid] = neg_inf();
+    return;
+  }
+  // Page j of the run; a prefetch past the run's end re-reads one token of its last page (valid
+  // = 1: every lane of a wave hits the same two rows), so every load in the loop is unconditional
+  // and the wait before each page counts exactly the page behind it.
+  auto page_valid = [&](int j) { return j < j1 ? min(kBlock, len - j * kBlock) : 1; };
+  auto load = [&](PageRegs<D>& r, int j) {
+    const int jc = min(j, j1 - 1);
+    const int64_t vp = jc == j0 ? pt0 : jc == j0 + 1 ? pt1 : pt[jc];
+    load_page<D>(r, kview + vp * page_stride, vview + vp * page_stride, (int)token_stride, page_valid(j), w, n,
+                 qd);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute it overlaps
+  };
+
+  u32x4 qf[KW];
+  const int nq = min(n, G - 1);
+#pragma unroll
+  for (int kw = 0; kw < KW; ++kw) qf[kw] = ld16(q + ((int64_t)rho * G + nq) * D + 32 * kw + 8 * qd);
+  PageRegs<D> ra, rb;
+  load(ra, j0);
+  load(rb, j0 + 1);
+  if (n >= G) {
+#pragma unroll
+    for (int kw = 0; kw < KW; ++kw) qf[kw] = zero4();
+  }
+  float m = neg_inf(), l = 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = fzero4();
+  for (int j = j0; j < j1; j += 2) {
+    attend_page<D>(ra, qf, page_valid(j), w, qd, scale_log2, m, l, acc);
+    load(ra, j + 2);
+    if (j + 1 < j1) attend_page<D>(rb, qf, page_valid(j + 1), w, qd, scale_log2, m, l, acc);
+    load(rb, j + 3);
+  }
+
+  // acc[c][ii] = O_w[head n][d = 32qd + 8ii + c] (unnormalized); combine the four waves
   if (qd == 0) { sm_m[w][n] = m; sm_l[w][n] = l; }
   if (n < G) {
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int d = 32 * qd + 8 * ii + c;
-        if (d < D) sm_o[w][n][d] = acc[c][ii];
+    for (int ii = 0; ii < 4; ++ii) {
+      const int d = 32 * qd + 8 * ii;
+      if (d < D) {
+        const f32x4 lo = {acc[0][ii], acc[1][ii], acc[2][ii], acc[3][ii]};
+        const f32x4 hi = {acc[4][ii], acc[5][ii], acc[6][ii], acc[7][ii]};
+        *reinterpret_cast<f32x4*>(&sm_o[w][n][d]) = lo;
+        *reinterpret_cast<f32x4*>(&sm_o[w][n][d + 4]) = hi;
       }
+    }
   }
   __syncthreads();
-  for (int e = tid; e < G * D; e += 256) {
-    const int h = e / D, d = e % D;
+  for (int e = tid; e < G * D / 4; e += 256) {
+    const int h = (4 * e) / D, d = (4 * e) % D;
     float M = neg_inf();
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][h]);
-    float num = 0.f, den = 0.f;
+    float den = 0.f;
+    f32x4 o = fzero4();
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
       const float mw = sm_m[ww][h];
       const float f = (mw == neg_inf()) ? 0.f : fast_exp2(mw - M);
-      num += f * sm_o[ww][h][d];
       den += f * sm_l[ww][h];
+      const f32x4 x = *reinterpret_cast<const f32x4*>(&sm_o[ww][h][d]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[t] += f * x[t];
     }
-    ws_o[(part * G + h) * D + d] = num / den;
-    if (d == 0) ws_lse[part * G + h] = (M + fast_log2(den)) * kLn2;
+    const float inv = 1.f / den;
+    const float lse = (M + fast_log2(den)) * kLn2;
+    if (nsplit == 1) {
+      uint2 pk;
+      pk.x = pack_bf2(o[0] * inv, o[1] * inv);
+      pk.y = pack_bf2(o[2] * inv, o[3] * inv);
+      *reinterpret_cast<uint2*>(out + ((int64_t)rho * G + h) * D + d) = pk;
+      if (d == 0 && lse_out) lse_out[(int64_t)rho * G + h] = lse;
+    } else {
+      f32x4 r = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+      *reinterpret_cast<f32x4*>(ws_o + (part * G + h) * D + d) = r;
+      if (d == 0) ws_lse[part * G + h] = lse;
+    }
+  }
+}
+
+// Merge of the decode splits: one workgroup per (row, head).  Thread (g, c) folds the parts
+// g, g + NG, ... of the 4-float chunk c into a running (max, sum, O); the NG folds of each chunk
+// are then combined through LDS.  Every thread's loads are independent of the other threads',
+// so even a few rows with many splits spread over the whole chip.  A part whose LSE is -inf
+// has weight 0 and is read from part 0 instead (split 0 always holds the row's first page).
+template <int D>
+__global__ __launch_bounds__(256) void k_merge_splits(int parts, int G, const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_lse, bf16* __restrict__ out,
+                                                      float* __restrict__ lse_out) {
+  constexpr int NC = D / 4;     // 4-float chunks per head
+  constexpr int NG = 256 / NC;  // part groups
+  __shared__ float s_m[NG][NC], s_s[NG][NC];
+  __shared__ f32x4 s_o[NG][NC];
+  const int64_t rh = blockIdx.x;  // row * G + head
+  const int64_t row = rh / G;
+  const int h = (int)(rh - row * G);
+  const int c = threadIdx.x % NC, g = threadIdx.x / NC;
+  const float* pl = part_lse + row * parts * G + h;
+  const float* po = part_o + (row * parts * G + h) * D + 4 * c;
+  float m = neg_inf(), sum = 0.f;
+  f32x4 o = fzero4();
+#pragma unroll 4
+  for (int j = g; j < parts; j += NG) {
+    const float x = pl[(int64_t)j * G];
+    const bool use = x != neg_inf();
+    const f32x4 v = *reinterpret_cast<const f32x4*>(po + (int64_t)(use ? j : 0) * G * D);
+    const float mn = fmaxf(m, x);
+    const float a = (m == neg_inf()) ? 0.f : __expf(m - mn);
+    const float wj = use ? __expf(x - mn) : 0.f;
+    sum = sum * a + wj;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = o[e] * a + wj * v[e];
+    m = mn;
+  }
+  s_m[g][c] = m;
+  s_s[g][c] = sum;
+  s_o[g][c] = o;
+  __syncthreads();
+  if (g == 0) {
+    float M = neg_inf();
+#pragma unroll
+    for (int t = 0; t < NG; ++t) M = fmaxf(M, s_m[t][c]);
+    float den = 0.f;
+    f32x4 acc = fzero4();
+#pragma unroll
+    for (int t = 0; t < NG; ++t) {
+      const float mt = s_m[t][c];
+      const float f = (mt == neg_inf()) ? 0.f : __expf(mt - M);
+      den += f * s_s[t][c];
+      const f32x4 ot = s_o[t][c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += f * ot[e];
+    }
+    const float inv = 1.f / den;
+    uint2 pk;
+    pk.x = pack_bf2(acc[0] * inv, acc[1] * inv);
+    pk.y = pack_bf2(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<uint2*>(out + rh * D + 4 * c) = pk;
+    if (lse_out && c == 0) lse_out[rh] = M + __logf(den);
   }
 }
 
@@ -150,7 +301,6 @@ __global__ __launch_bounds__(256) void k_lse_merge(int64_t rows, int parts, int 
   __shared__ float s_w[4][kMergeMaxPG];
   __shared__ float s_lse[4][16];
   __shared__ int s_parts[4][64];
-  __shared__ int s_np[4];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * 4 + wv;
   if (row >= rows) return;
@@ -221,21 +371,37 @@ __global__ __launch_bounds__(256) void k_lse_merge(int64_t rows, int parts, int 
   if (lse_out && lane < G) lse_out[row * G + lane] = s_lse[wv][lane];
 }
 
+int decode_splits(int rows, int k) {
+  int nsplit = std::min(k, std::max(1, (MSA_DECODE_TARGET_WGS + rows - 1) / rows));
+  const int ppw = (k + nsplit - 1) / nsplit;
+  return (k + ppw - 1) / ppw;
+}
+
 hipError_t launch_attn_decode(int rows, int G, int D, const void* q, const void* kview, const void* vview,
                               int64_t page_stride, int64_t token_stride, const int32_t* page_table, int k,
-                              const int32_t* row_len, float sm_scale, float* ws_o, float* ws_lse,
-                              hipStream_t stream) {
-  dim3 grid(k, rows), block(256);
+                              const int32_t* row_len, float sm_scale, void* out, float* lse, float* ws_o,
+                              float* ws_lse, hipStream_t stream) {
+  const int nsplit = decode_splits(rows, k);
+  const int ppw = (k + nsplit - 1) / nsplit;
+  dim3 grid(nsplit, rows), block(256);
   const float sl2 = sm_scale * kLog2e;
   const bf16* qq = static_cast<const bf16*>(q);
   const bf16* kk = static_cast<const bf16*>(kview);
   const bf16* vv = static_cast<const bf16*>(vview);
+  bf16* oo = static_cast<bf16*>(out);
   if (D == 128)
     hipLaunchKernelGGL(k_attn_decode<128>, grid, block, 0, stream, G, qq, kk, vv, page_stride, token_stride,
-                       page_table, k, row_len, sl2, ws_o, ws_lse);
+                       page_table, k, row_len, sl2, ppw, nsplit, oo, lse, ws_o, ws_lse);
   else
     hipLaunchKernelGGL(k_attn_decode<64>, grid, block, 0, stream, G, qq, kk, vv, page_stride, token_stride,
-                       page_table, k, row_len, sl2, ws_o, ws_lse);
+                       page_table, k, row_len, sl2, ppw, nsplit, oo, lse, ws_o, ws_lse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  const dim3 mgrid((unsigned)((int64_t)rows * G));
+  if (D == 128)
+    hipLaunchKernelGGL(k_merge_splits<128>, mgrid, dim3(256), 0, stream, nsplit, G, ws_o, ws_lse, oo, lse);
+  else
+    hipLaunchKernelGGL(k_merge_splits<64>, mgrid, dim3(256), 0, stream, nsplit, G, ws_o, ws_lse, oo, lse);
   return hipGetLastError();
 }
 
@@ -244,14 +410,6 @@ hipError_t launch_lse_merge_bf16(int64_t rows, int parts, int G, int D, const vo
   const int64_t wgs = (rows + 3) / 4;
   hipLaunchKernelGGL(k_lse_merge<bf16>, dim3((unsigned)wgs), dim3(256), 0, stream, rows, parts, G, D,
                      static_cast<const bf16*>(part_o), part_lse, static_cast<bf16*>(out), lse_out);
-  return hipGetLastError();
-}
-
-hipError_t launch_lse_merge_f32(int64_t rows, int parts, int G, int D, const float* part_o, const float* part_lse,
-                                void* out, float* lse_out, hipStream_t stream) {
-  const int64_t wgs = (rows + 3) / 4;
-  hipLaunchKernelGGL(k_lse_merge<float>, dim3((unsigned)wgs), dim3(256), 0, stream, rows, parts, G, D, part_o,
-                     part_lse, static_cast<bf16*>(out), lse_out);
   return hipGetLastError();
 }
 

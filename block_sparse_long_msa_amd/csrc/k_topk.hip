@@ -2,11 +2,16 @@
 //
 // Top-k (Chinese page of the MiniMax-M3 serving write-up, sections "MiniMax稀疏注意力改变了服务问题"
 // and "遗留问题"): the k best candidate blocks by score; equal scores prefer the lower block
-// id; output in ascending block id with -1 padding.  One wavefront per row runs a radix
-// select on order-preserving 32-bit keys: it skips the bits every candidate shares, then
-// takes 8-bit digits from the top with an LDS histogram per pass, stopping as soon as the
-// boundary digit's bucket is taken whole.  A final in-order ballot pass writes the chosen
-// ids, which gives ascending order and the lower-id tie rule for free.
+// id; output in ascending block id with -1 padding.  Both kernels work on order-preserving
+// 32-bit keys and end with an in-order ballot pass that writes the chosen ids, which gives
+// ascending order and the lower-id tie rule for free.
+//   k_topk (many rows, or rows too long for registers): radix select; it skips the bits every
+//     candidate shares, then takes 8-bit digits from the top with an LDS histogram per pass,
+//     stopping as soon as the boundary digit's bucket is taken whole.
+//   k_topk_reg (few rows, decode): the row sits in registers and the k-th largest key is found
+//     by bisection with ballot counts.
+#include <type_traits>
+
 #include "msa_device.h"
 
 namespace msa {
@@ -148,6 +153,171 @@ __global__ __launch_bounds__(64 * NW) void k_topk(int B, int Hkv, int max_blocks
   if (tid == 0) cnt[row] = written;
 }
 
+// The same selection for rows whose candidates fit in registers (64*NW*R >= n): every lane
+// reads its R scores once, and the k-th largest key T is found bit by bit from the highest bit
+// the keys do not all share, counting the keys at or above each trial threshold with ballots.
+// T is the largest value with at least k keys >= T, so fewer than k keys are > T and the
+// boundary ties are taken in id order exactly as above.  Used when there are few rows (decode),
+// where the radix passes' round trips through memory and LDS dominate.
+//
+// With page_table != NULL the same launch also writes the row's decode page table and row length
+// (as k_page_table below), from the chosen ids kept in LDS; the request lookup is issued at the
+// start so that it overlaps the score loads.
+struct PageTableOut {
+  int B;
+  const int32_t* block_table;
+  const int32_t* ctx_len;
+  const int32_t* cu_q;
+  int32_t* page_table;  // NULL: top-k only
+  int32_t* row_len;
+};
+
+template <int NW, int R>
+__global__ __launch_bounds__(64 * NW) void k_topk_reg(int Hkv, int max_blocks, const int32_t* __restrict__ q_pos,
+                                                      const float* __restrict__ scores, int k,
+                                                      int32_t* __restrict__ sel, int32_t* __restrict__ cnt,
+                                                      PageTableOut pto) {
+  constexpr int NT = 64 * NW;
+  __shared__ uint32_t s_c[2][NW];
+  __shared__ uint32_t s_r[2][NW];
+  __shared__ int s_sel[64];
+  const int row = blockIdx.x;  // t*Hkv + g
+  const int t = row / Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int pos = q_pos[t];
+  const int n = min(pos / kBlock + 1, max_blocks);
+  const float* s = scores + (int64_t)row * max_blocks;
+  int32_t* out = sel + (int64_t)row * k;
+  // id i = tid + NT*r.  All R loads are unconditional (clamped to the row's max_blocks entries)
+  // and go out together with the row's position and the request lookup for the page table.
+  float v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] = s[min(tid + NT * r, max_blocks - 1)];
+  int r_req = 0, lim = 0;
+  if (pto.page_table) {
+    int L;
+    request_and_len(pto.cu_q, pto.ctx_len, pto.B, t, r_req, L);
+    lim = min(pos + 1, L);  // tokens s < lim are valid
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) asm volatile("" ::"v"(v[r]));
+  // the chosen ids in ascending order, c of them, also kept in s_sel[0 .. c-1]
+  auto page_table = [&](int c) {
+    __syncthreads();
+    if (wv == 0) {
+      const int g = row - t * Hkv;
+      int v = -1, len = 0;
+      if (lane < c) {
+        const int bl = s_sel[lane];
+        v = pto.block_table[(int64_t)r_req * max_blocks + bl] * (kBlock * Hkv) + g;
+        len = min(kBlock, lim - bl * kBlock);
+      }
+      if (lane < k) pto.page_table[(int64_t)row * k + lane] = v;
+#pragma unroll
+      for (int m = 1; m < kWave; m <<= 1) len += __shfl_xor(len, m, kWave);
+      if (lane == 0) pto.row_len[row] = len;
+    }
+  };
+  if (n <= k) {
+    for (int i = tid; i < k; i += NT) {
+      out[i] = i < n ? i : -1;
+      s_sel[i] = i;
+    }
+    if (tid == 0) cnt[row] = n;
+    if (pto.page_table) page_table(n);
+    return;
+  }
+  // ids >= n get key 0, below every candidate key (candidate scores are finite)
+  uint32_t key[R];
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const bool in = tid + NT * r < n;
+    const uint32_t kr = order_key(v[r]);
+    key[r] = in ? kr : 0u;
+    kmin = min(kmin, in ? kr : 0xffffffffu);
+    kmax = max(kmax, key[r]);
+  }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, m, kWave));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m, kWave));
+  }
+  if (NW > 1) {
+    if (lane == 0) { s_r[0][wv] = kmin; s_r[1][wv] = kmax; }
+    __syncthreads();
+    for (int x = 0; x < NW; ++x) { kmin = min(kmin, s_r[0][x]); kmax = max(kmax, s_r[1][x]); }
+  }
+  // counts of keys >= thr over the whole row (uniform result)
+  auto count_ge = [&](uint32_t thr, int parity) -> int {
+    int c = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) c += __popcll(__ballot(key[r] >= thr));
+    if (NW > 1) {
+      if (lane == 0) s_c[parity][wv] = c;
+      __syncthreads();
+      c = 0;
+      for (int x = 0; x < NW; ++x) c += s_c[parity][x];
+    }
+    return c;
+  };
+  uint32_t T = kmin;
+  if (kmin != kmax) {
+    const int hb = 31 - __builtin_clz(kmin ^ kmax);
+    T = hb == 31 ? 0u : (kmin & ~((2u << hb) - 1u));
+    for (int b = hb; b >= 0; --b) {  // every trial threshold is >= 1, so id slots past n never count
+      const uint32_t cand = T | (1u << b);
+      if (count_ge(cand, b & 1) >= k) T = cand;
+    }
+  }
+  // parity 1: the last bisection step (b = 0) used buffer 0, which a slow wave may still be reading
+  const int remaining = k - (T == 0xffffffffu ? 0 : count_ge(T + 1u, 1));
+
+  // emit in id order: keys above T, then the first `remaining` keys equal to T
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int written = 0, ties_seen = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = tid + NT * r;
+    const bool gt = key[r] > T;
+    const bool eq = i < n && key[r] == T;
+    const uint64_t eqm = __ballot(eq);
+    int eq_before = ties_seen + __popcll(eqm & lt_mask);
+    int eq_all = __popcll(eqm);
+    if (NW > 1) {
+      __syncthreads();  // s_c of the previous use is read by every wave
+      if (lane == 0) s_c[0][wv] = eq_all;
+      __syncthreads();
+      eq_all = 0;
+      for (int x = 0; x < NW; ++x) {
+        if (x < wv) eq_before += s_c[0][x];
+        eq_all += s_c[0][x];
+      }
+    }
+    const bool take = gt || (eq && eq_before < remaining);
+    const uint64_t tm = __ballot(take);
+    int slot = written + __popcll(tm & lt_mask);
+    int take_all = __popcll(tm);
+    if (NW > 1) {
+      if (lane == 0) s_c[1][wv] = take_all;
+      __syncthreads();
+      take_all = 0;
+      for (int x = 0; x < NW; ++x) {
+        if (x < wv) slot += s_c[1][x];
+        take_all += s_c[1][x];
+      }
+    }
+    if (take && slot < k) {
+      out[slot] = i;
+      s_sel[slot] = i;
+    }
+    written += take_all;
+    ties_seen += eq_all;
+  }
+  if (tid == 0) cnt[row] = k;
+  if (pto.page_table) page_table(k);
+}
+
 // Decode sparse page table over the strided view (Chinese page, section "MSA需要新的分页注意力集成"):
 // row rho = t*Hkv + g, page_table[rho, j] = block_table[r, sel[t,g,j]] * 128 * Hkv + g.
 // One wavefront per row; lane j handles slot j (k <= 64), row_len is a wave sum.
@@ -162,8 +332,9 @@ __global__ __launch_bounds__(256) void k_page_table(int rows, int B, int Hkv, in
   const int j = threadIdx.x & 63;
   if (rho >= rows) return;
   const int t = rho / Hkv, g = rho % Hkv;
-  const int r = request_of(cu_q, B, t);
-  const int lim = min(q_pos[t] + 1, ctx_len[r]);  // tokens s < lim are valid
+  int r, L;
+  request_and_len(cu_q, ctx_len, B, t, r, L);
+  const int lim = min(q_pos[t] + 1, L);  // tokens s < lim are valid
   const int c = cnt[rho];
   int v = -1, len = 0;
   if (j < c) {
@@ -177,18 +348,49 @@ __global__ __launch_bounds__(256) void k_page_table(int rows, int B, int Hkv, in
   if (j == 0) row_len[rho] = len;
 }
 
+#ifndef MSA_TOPK_REG_MAX_ROWS
+#define MSA_TOPK_REG_MAX_ROWS 4096  // register top-k below this many rows, radix passes above
+#endif
+
+template <int NW, int R>
+static void launch_reg(int rows, hipStream_t stream, int Hkv, int max_blocks, const int32_t* q_pos,
+                       const float* scores, int k, int32_t* sel, int32_t* cnt, const PageTableOut& pto) {
+  hipLaunchKernelGGL((k_topk_reg<NW, R>), dim3(rows), dim3(64 * NW), 0, stream, Hkv, max_blocks, q_pos, scores, k,
+                     sel, cnt, pto);
+}
+
+// Top-k, and with pto.page_table set also the decode page table.  Returns false (nothing
+// launched) when the shape needs the radix kernel, which does not build page tables.
+static bool launch_topk_reg(int rows, int Hkv, int max_blocks, const int32_t* q_pos, const float* scores, int k,
+                            int32_t* sel, int32_t* cnt, const PageTableOut& pto, hipStream_t stream) {
+  if (rows >= MSA_TOPK_REG_MAX_ROWS || max_blocks > 16384) return false;
+  // the smallest register layout that holds a row: 64*NW*R >= max_blocks
+  auto go = [&](auto nw, auto r) {
+    launch_reg<decltype(nw)::value, decltype(r)::value>(rows, stream, Hkv, max_blocks, q_pos, scores, k, sel, cnt,
+                                                        pto);
+  };
+  using std::integral_constant;
+  if (max_blocks <= 64) go(integral_constant<int, 1>(), integral_constant<int, 1>());
+  else if (max_blocks <= 128) go(integral_constant<int, 1>(), integral_constant<int, 2>());
+  else if (max_blocks <= 256) go(integral_constant<int, 1>(), integral_constant<int, 4>());
+  else if (max_blocks <= 512) go(integral_constant<int, 1>(), integral_constant<int, 8>());
+  else if (max_blocks <= 1024) go(integral_constant<int, 1>(), integral_constant<int, 16>());
+  else if (max_blocks <= 2048) go(integral_constant<int, 4>(), integral_constant<int, 8>());
+  else if (max_blocks <= 4096) go(integral_constant<int, 4>(), integral_constant<int, 16>());
+  else if (max_blocks <= 8192) go(integral_constant<int, 16>(), integral_constant<int, 8>());
+  else go(integral_constant<int, 16>(), integral_constant<int, 16>());
+  return true;
+}
+
 hipError_t launch_topk(int B, int Nq, int Hkv, int max_blocks, const int32_t* cu_q, const int32_t* q_pos,
                        const float* scores, int k, int32_t* sel, int32_t* cnt, hipStream_t stream) {
-  // few long rows: a workgroup of up to 16 waves per row; many rows: one wave each
   const int rows = Nq * Hkv;
-  const int want = rows >= 4096 ? 1 : (max_blocks >= 4096 ? 16 : (max_blocks >= 1024 ? 4 : 1));
-  if (want == 16)
+  const PageTableOut none{B, nullptr, nullptr, cu_q, nullptr, nullptr};
+  if (launch_topk_reg(rows, Hkv, max_blocks, q_pos, scores, k, sel, cnt, none, stream)) return hipGetLastError();
+  if (rows < MSA_TOPK_REG_MAX_ROWS)  // few rows longer than the register layouts: 16 waves per row
     hipLaunchKernelGGL(k_topk<16>, dim3(rows), dim3(1024), 0, stream, B, Hkv, max_blocks, cu_q, q_pos, scores, k,
                        sel, cnt);
-  else if (want == 4)
-    hipLaunchKernelGGL(k_topk<4>, dim3(rows), dim3(256), 0, stream, B, Hkv, max_blocks, cu_q, q_pos, scores, k, sel,
-                       cnt);
-  else
+  else  // many rows: radix passes, one wave per row
     hipLaunchKernelGGL(k_topk<1>, dim3(rows), dim3(64), 0, stream, B, Hkv, max_blocks, cu_q, q_pos, scores, k, sel,
                        cnt);
   return hipGetLastError();
@@ -201,6 +403,18 @@ hipError_t launch_page_table(int B, int Nq, int Hkv, int max_blocks, const int32
   hipLaunchKernelGGL(k_page_table, dim3((rows + 3) / 4), dim3(256), 0, stream, rows, B, Hkv, max_blocks,
                      block_table, ctx_len, cu_q, q_pos, sel, cnt, k, page_table, row_len);
   return hipGetLastError();
+}
+
+hipError_t launch_topk_page_table(int B, int Nq, int Hkv, int max_blocks, const int32_t* block_table,
+                                  const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos,
+                                  const float* scores, int k, int32_t* sel, int32_t* cnt, int32_t* page_table,
+                                  int32_t* row_len, hipStream_t stream) {
+  const PageTableOut pto{B, block_table, ctx_len, cu_q, page_table, row_len};
+  if (launch_topk_reg(Nq * Hkv, Hkv, max_blocks, q_pos, scores, k, sel, cnt, pto, stream)) return hipGetLastError();
+  hipError_t e = launch_topk(B, Nq, Hkv, max_blocks, cu_q, q_pos, scores, k, sel, cnt, stream);
+  if (e != hipSuccess) return e;
+  return launch_page_table(B, Nq, Hkv, max_blocks, block_table, ctx_len, cu_q, q_pos, sel, cnt, k, page_table,
+                           row_len, stream);
 }
 
 }  // namespace msa

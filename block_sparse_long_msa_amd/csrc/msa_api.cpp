@@ -25,14 +25,16 @@ hipError_t launch_topk(int B, int Nq, int Hkv, int max_blocks, const int32_t* cu
 hipError_t launch_page_table(int B, int Nq, int Hkv, int max_blocks, const int32_t* block_table,
                              const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const int32_t* sel,
                              const int32_t* cnt, int k, int32_t* page_table, int32_t* row_len, hipStream_t stream);
+hipError_t launch_topk_page_table(int B, int Nq, int Hkv, int max_blocks, const int32_t* block_table,
+                                  const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos,
+                                  const float* scores, int k, int32_t* sel, int32_t* cnt, int32_t* page_table,
+                                  int32_t* row_len, hipStream_t stream);
 hipError_t launch_attn_decode(int rows, int G, int D, const void* q, const void* kview, const void* vview,
                               int64_t page_stride, int64_t token_stride, const int32_t* page_table, int k,
-                              const int32_t* row_len, float sm_scale, float* ws_o, float* ws_lse,
-                              hipStream_t stream);
+                              const int32_t* row_len, float sm_scale, void* out, float* lse, float* ws_o,
+                              float* ws_lse, hipStream_t stream);
 hipError_t launch_lse_merge_bf16(int64_t rows, int parts, int G, int D, const void* part_o, const float* part_lse,
                                  void* out, float* lse_out, hipStream_t stream);
-hipError_t launch_lse_merge_f32(int64_t rows, int parts, int G, int D, const float* part_o, const float* part_lse,
-                                void* out, float* lse_out, hipStream_t stream);
 size_t prefill_workspace_bytes(int32_t Nq, int32_t Hkv, int32_t k, int32_t B, int32_t max_blocks);
 hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blocks, const int32_t* block_table,
                                const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const void* q,
@@ -221,6 +223,31 @@ msa_status msa_build_sparse_page_table(const msa_batch* batch, int32_t num_kv_he
                   "msa_build_sparse_page_table launch");
 }
 
+msa_status msa_topk_page_table(const msa_batch* batch, int32_t num_kv_heads, int32_t num_pages,
+                               const float* scores, int32_t k, int32_t* sel, int32_t* cnt, int32_t* page_table,
+                               int32_t* row_len, msa_stream_t stream) {
+  g_last_error.clear();
+  if (msa_status s = check_batch(batch)) return s;
+  MSA_REQUIRE(num_kv_heads >= 1 && num_kv_heads <= kMaxHkv, MSA_ERR_UNSUPPORTED, "num_kv_heads must be in [1, %d]",
+              kMaxHkv);
+  MSA_REQUIRE(k >= 1 && k <= kMaxK, MSA_ERR_UNSUPPORTED, "k must be in [1, %d], got %d", kMaxK, k);
+  MSA_REQUIRE(num_pages >= 1, MSA_ERR_INVALID_ARG, "num_pages must be >= 1");
+  MSA_REQUIRE((int64_t)num_pages * 128 * num_kv_heads <= 0x7fffffffLL, MSA_ERR_UNSUPPORTED,
+              "num_pages*128*num_kv_heads must fit in int32 (virtual page ids)");
+  MSA_REQUIRE(batch->num_queries == 0 || (scores && sel && cnt && page_table && row_len), MSA_ERR_INVALID_ARG,
+              "scores, sel, cnt, page_table and row_len must be non-NULL");
+  MSA_REQUIRE(aligned4(scores) && aligned4(sel) && aligned4(cnt) && aligned4(page_table) && aligned4(row_len),
+              MSA_ERR_INVALID_ARG, "arrays must be 4-byte aligned");
+  MSA_REQUIRE((int64_t)batch->num_queries * num_kv_heads <= 0x7fffffff, MSA_ERR_UNSUPPORTED,
+              "num_queries * num_kv_heads exceeds the grid limit");
+  if (batch->num_queries == 0) return MSA_OK;
+  return from_hip(msa::launch_topk_page_table(batch->num_requests, batch->num_queries, num_kv_heads,
+                                              batch->max_blocks, batch->block_table, batch->ctx_len, batch->cu_q,
+                                              batch->q_pos, scores, k, sel, cnt, page_table, row_len,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                  "msa_topk_page_table launch");
+}
+
 size_t msa_sparse_attn_decode_workspace_size(int32_t rows, int32_t G, int32_t D, int32_t k) {
   if (rows <= 0 || G <= 0 || D <= 0 || k <= 0) return 0;
   const size_t parts = (size_t)rows * k * G;
@@ -247,6 +274,7 @@ msa_status msa_sparse_attn_decode(int32_t rows, int32_t G, int32_t D, const void
   MSA_REQUIRE(aligned4(page_table) && aligned4(row_len) && aligned4(lse), MSA_ERR_INVALID_ARG,
               "page_table, row_len and lse must be 4-byte aligned");
   MSA_REQUIRE(rows <= kMaxGridY, MSA_ERR_UNSUPPORTED, "rows must be <= %d", kMaxGridY);
+  MSA_REQUIRE(token_stride * 128 + D <= 0x7fffffffLL, MSA_ERR_UNSUPPORTED, "token_stride*128 must fit in int32");
   const size_t need = msa_sparse_attn_decode_workspace_size(rows, G, D, k);
   MSA_REQUIRE(workspace_bytes >= need, MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
               workspace_bytes);
@@ -254,11 +282,9 @@ msa_status msa_sparse_attn_decode(int32_t rows, int32_t G, int32_t D, const void
   float* ws_o = static_cast<float*>(workspace);
   float* ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(parts * D * sizeof(float)));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = msa::launch_attn_decode(rows, G, D, q, k_base, v_base, page_stride, token_stride, page_table, k,
-                                         row_len, sm_scale, ws_o, ws_lse, st);
-  if (e != hipSuccess) return from_hip(e, "msa_sparse_attn_decode launch");
-  return from_hip(msa::launch_lse_merge_f32(rows, k, G, D, ws_o, ws_lse, out, lse, st),
-                  "msa_sparse_attn_decode merge launch");
+  return from_hip(msa::launch_attn_decode(rows, G, D, q, k_base, v_base, page_stride, token_stride, page_table, k,
+                                          row_len, sm_scale, out, lse, ws_o, ws_lse, st),
+                  "msa_sparse_attn_decode launch");
 }
 
 size_t msa_sparse_attn_prefill_workspace_size(const msa_batch* batch, int32_t num_kv_heads, int32_t k) {

@@ -87,4 +87,25 @@ __device__ __forceinline__ int request_of(const int32_t* __restrict__ cu_q, int 
   return lo;
 }
 
+// The same request index r, and ctx_len[r], found by one wavefront with one round of loads per
+// 64 requests instead of a chain of dependent loads: the requests whose first query row is
+// <= t form a prefix (cu_q is non-decreasing), and r is its last element.  Every lane of the
+// wave must call it; the results are uniform.
+__device__ __forceinline__ void request_and_len(const int32_t* __restrict__ cu_q,
+                                                const int32_t* __restrict__ ctx_len, int B, int t, int& r,
+                                                int& len) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int count = 0, l_last = 0;
+  for (int base = 0; base < B; base += kWave) {
+    const int i = min(base + lane, B - 1);
+    const int c = cu_q[i], l = ctx_len[i];
+    asm volatile("" ::"v"(c), "v"(l));  // both loads in the same round trip
+    const uint64_t m = __ballot(base + lane < B && c <= t);
+    if (m) l_last = __shfl(l, 63 - __builtin_clzll(m), kWave);
+    count += __popcll(m);
+  }
+  r = count - 1;
+  len = __builtin_amdgcn_readfirstlane(l_last);
+}
+
 }  // namespace msa

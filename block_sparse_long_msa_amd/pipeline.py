@@ -1,6 +1,6 @@
 """One MSA layer invocation as a chain of C-ABI calls with preallocated buffers.
 
-MSADecode: index scores -> top-k -> sparse page table -> decode attention (split over pages,
+MSADecode: index scores -> top-k + sparse page table -> decode attention (split over pages,
            merged in the library).
 MSAPrefill: index scores -> top-k -> KV-block-major attention (partials) -> LSE merge.
 
@@ -12,13 +12,19 @@ import torch
 
 from . import (Batch, msa_build_sparse_page_table, msa_index_score, msa_index_topk, msa_index_topk_workspace_size,
                msa_lse_merge, msa_sparse_attn_decode, msa_sparse_attn_decode_workspace_size,
-               msa_sparse_attn_prefill, msa_sparse_attn_prefill_workspace_size, msa_topk_blocks)
+               msa_sparse_attn_prefill, msa_sparse_attn_prefill_workspace_size, msa_topk_blocks,
+               msa_topk_page_table)
 
 
 class MSADecode:
-    def __init__(self, batch: Batch, Hkv: int, G: int, D: int, k: int, num_pages: int, device="cuda"):
+    """``fused_select`` (default) runs top-k and the page table as one call (msa_topk_page_table);
+    ``False`` runs msa_topk_blocks and msa_build_sparse_page_table.  Both give identical results."""
+
+    def __init__(self, batch: Batch, Hkv: int, G: int, D: int, k: int, num_pages: int, device="cuda",
+                 fused_select: bool = True):
         Nq, mb = batch.num_queries, batch.max_blocks
         self.batch, self.Hkv, self.G, self.D, self.k, self.num_pages = batch, Hkv, G, D, k, num_pages
+        self.fused_select = fused_select
         self.rows = Nq * Hkv
         self.scores = torch.empty((Nq, Hkv, mb), dtype=torch.float32, device=device)
         self.sel = torch.empty((Nq, Hkv, k), dtype=torch.int32, device=device)
@@ -34,9 +40,13 @@ class MSADecode:
         msa_index_score(self.batch, q_idx, kidx, self.scores, stream)
 
     def select(self, stream=None):
-        msa_topk_blocks(self.batch, self.Hkv, self.scores, self.k, self.sel, self.cnt, stream)
-        msa_build_sparse_page_table(self.batch, self.Hkv, self.num_pages, self.sel, self.cnt, self.k,
-                                    self.page_table, self.row_len, stream)
+        if self.fused_select:
+            msa_topk_page_table(self.batch, self.Hkv, self.num_pages, self.scores, self.k, self.sel, self.cnt,
+                                self.page_table, self.row_len, stream)
+        else:
+            msa_topk_blocks(self.batch, self.Hkv, self.scores, self.k, self.sel, self.cnt, stream)
+            msa_build_sparse_page_table(self.batch, self.Hkv, self.num_pages, self.sel, self.cnt, self.k,
+                                        self.page_table, self.row_len, stream)
 
     def attend(self, q, kcache, vcache, sm_scale: float, stream=None):
         msa_sparse_attn_decode(self.rows, self.G, self.D, q, kcache, vcache, self.D, self.Hkv * self.D,

@@ -125,6 +125,14 @@ msa_status msa_build_sparse_page_table(const msa_batch* batch, int32_t num_kv_he
                                        const int32_t* sel, const int32_t* cnt, int32_t k,
                                        int32_t* page_table, int32_t* row_len, msa_stream_t stream);
 
+/* msa_topk_blocks followed by msa_build_sparse_page_table, in one launch when the rows fit the
+ * register top-k (fewer than 4096 rows of at most 16384 blocks; decode shapes), else in two.
+ * Same arguments, outputs and results as the two calls; the fusion is the one the pages name as
+ * open for MSA's small kernels (Chinese page, section "遗留问题"). */
+msa_status msa_topk_page_table(const msa_batch* batch, int32_t num_kv_heads, int32_t num_pages,
+                               const float* scores, int32_t k, int32_t* sel, int32_t* cnt, int32_t* page_table,
+                               int32_t* row_len, msa_stream_t stream);
+
 /* Decode attention over the sparse page table (same section): each row rho attends with its
  * G query heads q[rho*G .. rho*G+G-1] to the first row_len[rho] tokens of its virtual pages.
  * Token i of row rho is virtual page v = page_table[rho, i/128], slot s = i%128, and its

@@ -69,6 +69,16 @@ def page_table(dev, b, sel, cnt, k=None):
     return pt, rl
 
 
+def topk_page_table(dev, b, s, k=None):
+    """msa_topk_page_table: top-k and the page table in one call."""
+    wl = dev.wl
+    k = k or wl.k
+    sel, cnt = poison_i32(wl.Nq, wl.Hkv, k), poison_i32(wl.Nq, wl.Hkv)
+    pt, rl = poison_i32(wl.Nq * wl.Hkv, k), poison_i32(wl.Nq * wl.Hkv)
+    lib().msa_topk_page_table(b, wl.Hkv, dev.kcache.shape[0], s, k, sel, cnt, pt, rl)
+    return sel, cnt, pt, rl
+
+
 def decode_attention(dev, pt, rl, k=None):
     wl = dev.wl
     k = k or wl.k

@@ -96,12 +96,28 @@ def test_page_table_rejects_overflowing_virtual_ids(lib):
 
 
 @no_gpu
+@pytest.mark.parametrize("hkv,pages,k,status", [(2, 8, 0, UNSUPPORTED), (2, 8, 65, UNSUPPORTED),
+                                                (0, 8, 4, UNSUPPORTED), (2, 0, 4, INVALID),
+                                                (8, 1 << 22, 16, UNSUPPORTED)])
+def test_topk_page_table_rejects(lib, hkv, pages, k, status):
+    b = _batch()
+    assert lib.msa_topk_page_table(ctypes.byref(b), hkv, pages, FAKE, k, FAKE, FAKE, FAKE, FAKE, None) == status
+
+
+@no_gpu
+def test_topk_page_table_rejects_null_outputs(lib):
+    b = _batch()
+    assert lib.msa_topk_page_table(ctypes.byref(b), 2, 8, FAKE, 4, FAKE, FAKE, None, FAKE, None) == INVALID
+
+
+@no_gpu
 @pytest.mark.parametrize("G,D,ps,ts,k,ws,status", [
     (3, 128, 128, 1024, 16, 1 << 30, UNSUPPORTED),
     (8, 96, 96, 768, 16, 1 << 30, UNSUPPORTED),
     (8, 128, 100, 1024, 16, 1 << 30, INVALID),      # page stride not a multiple of 8 elements
     (8, 128, 128, 1024, 0, 1 << 30, UNSUPPORTED),
     (8, 128, 128, 1024, 16, 64, WS_SMALL),
+    (8, 128, 128, 1 << 24, 16, 1 << 30, UNSUPPORTED),   # token_stride*128 beyond int32
 ])
 def test_decode_attention_rejects(lib, G, D, ps, ts, k, ws, status):
     st = lib.msa_sparse_attn_decode(4, G, D, FAKE, FAKE, FAKE, ps, ts, FAKE, k, FAKE, 0.1, FAKE, FAKE, FAKE, ws, None)
@@ -131,6 +147,7 @@ def test_empty_inputs_launch_nothing(lib):
     b = _batch(Nq=0)
     assert lib.msa_index_score(ctypes.byref(b), None, _cache(), None, None) == OK
     assert lib.msa_topk_blocks(ctypes.byref(b), 2, None, 4, None, None, None) == OK
+    assert lib.msa_topk_page_table(ctypes.byref(b), 2, 8, None, 4, None, None, None, None, None) == OK
     assert lib.msa_lse_merge(0, 4, 8, 128, None, None, None, None, None) == OK
     assert lib.msa_sparse_attn_decode(0, 8, 128, None, None, None, 128, 1024, None, 4, None, 0.1, None, None, None,
                                       0, None) == OK

@@ -12,7 +12,7 @@ import torch
 
 import msa_inputs as mi
 import oracle
-from _gpu import announce, batch, decode_attention, host, lib, page_table, scores, setup, topk
+from _gpu import announce, batch, decode_attention, host, lib, page_table, scores, setup, topk, topk_page_table
 from _helpers import assert_attn_close, np_inputs, selection_excused
 
 pytestmark = pytest.mark.gpu
@@ -27,9 +27,14 @@ CASES = {
     "g1_d128": dict(ctx=[1800, 900], nq=[1, 1], Hq=4, Hkv=4, D=128, Di=128, k=3),
     # Hkv * Di > 1024: the decode scorer's direct-to-register variant
     "hkv16_direct_scorer": dict(ctx=[900, 400], nq=[1, 2], Hq=32, Hkv=16, D=64, Di=128, k=3),
-    # few long rows: top-k runs 16 (>= 4096 blocks) and 4 (>= 1024 blocks) waves per row
+    # few long rows: the register top-k holds a row in 16 waves (> 4096 blocks) or 4 waves (> 1024)
     "topk_16_waves": dict(ctx=[524300, 300001], nq=[1, 1], Hq=4, Hkv=1, D=64, Di=64, k=20),
     "topk_4_waves": dict(ctx=[190000, 140000], nq=[1, 1], Hq=8, Hkv=2, D=64, Di=64, k=33),
+    # one wave holding 4 and 8 scores per lane (up to 256 / 512 blocks)
+    "topk_4_per_lane": dict(ctx=[30000, 700], nq=[1, 2], Hq=8, Hkv=2, D=64, Di=64, k=7),
+    "topk_8_per_lane": dict(ctx=[60000, 33000], nq=[1, 1], Hq=8, Hkv=2, D=64, Di=64, k=64),
+    # >= 4096 rows: the radix-pass top-k
+    "many_rows_radix": dict(ctx=[3000] * 2 + [700] * 254, nq=[1] * 256, Hq=32, Hkv=16, D=64, Di=64, k=6),
 }
 
 
@@ -44,6 +49,9 @@ def _run(dev, max_q=None):
     s = scores(dev, b)
     sel, cnt = topk(dev, b, s)
     pt, rl = page_table(dev, b, sel, cnt)
+    # the one-call form gives the same four arrays bit for bit
+    for a, f in zip((sel, cnt, pt, rl), topk_page_table(dev, b, s)):
+        assert torch.equal(a, f), "msa_topk_page_table differs from msa_topk_blocks + msa_build_sparse_page_table"
     out, lse = decode_attention(dev, pt, rl)
     return s, sel, cnt, pt, rl, out, lse
 
