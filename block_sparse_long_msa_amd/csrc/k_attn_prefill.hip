@@ -201,21 +201,36 @@ __global__ __launch_bounds__(256, 2) void k_attn_kvbm(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, qd = lane >> 4;
 
   // ---- stage K (row-major) and V (transposed) of block b, KV head g ----
+  // Tokens past the block's end (the context's last, partial block) read the last token that
+  // exists instead: every load is in bounds and unconditional, so all of them are in flight at
+  // once, and the values are finite.  Those keys are masked for every query row (lim <= in_block),
+  // so their scores never count and their V rows are weighted by exactly 0.
   const bf16* kg = kcache + ((int64_t)page * kBlock * Hkv + g) * D;
   const bf16* vg = vcache + ((int64_t)page * kBlock * Hkv + g) * D;
-  const int64_t tstride = (int64_t)Hkv * D;
+  const int tstride = Hkv * D;
+  constexpr int NKL = kBlock * D / 8 / 256, NVL = kBlock * D / 16 / 256;
+  u32x4 kst[NKL], vst[NVL][2];
 #pragma unroll
-  for (int c = 0; c < kBlock * D / 8 / 256; ++c) {
-    const int idx = tid + 256 * c, tok = idx / (D / 8), ch = idx % (D / 8);
-    const u32x4 v = tok < in_block ? ld16(kg + tok * tstride + ch * 8) : zero4();
-    st16(&k_lds[tok * KST + ch * 8], v);
+  for (int c = 0; c < NKL; ++c) {
+    const int idx = tid + 256 * c, tok = min(idx / (D / 8), in_block - 1), ch = idx % (D / 8);
+    kst[c] = ld16(kg + tok * tstride + ch * 8);
   }
 #pragma unroll
-  for (int c = 0; c < kBlock * D / 16 / 256; ++c) {  // two tokens per lane -> 32-bit transposed writes
+  for (int c = 0; c < NVL; ++c) {
+    const int idx = tid + 256 * c, tp = idx % (kBlock / 2), ch = idx / (kBlock / 2);
+    vst[c][0] = ld16(vg + min(2 * tp, in_block - 1) * tstride + ch * 8);
+    vst[c][1] = ld16(vg + min(2 * tp + 1, in_block - 1) * tstride + ch * 8);
+  }
+#pragma unroll
+  for (int c = 0; c < NKL; ++c) {
+    const int idx = tid + 256 * c, tok = idx / (D / 8), ch = idx % (D / 8);
+    st16(&k_lds[tok * KST + ch * 8], kst[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < NVL; ++c) {  // two tokens per lane -> 32-bit transposed writes
     const int idx = tid + 256 * c, tp = idx % (kBlock / 2), ch = idx / (kBlock / 2);
     const int t0 = 2 * tp;
-    const u32x4 a = t0 < in_block ? ld16(vg + t0 * tstride + ch * 8) : zero4();
-    const u32x4 bb = t0 + 1 < in_block ? ld16(vg + (t0 + 1) * tstride + ch * 8) : zero4();
+    const u32x4 a = vst[c][0], bb = vst[c][1];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t lo = (a[e] & 0xffffu) | (bb[e] << 16);           // d = 8ch + 2e

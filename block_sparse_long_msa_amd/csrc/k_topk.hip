@@ -5,11 +5,11 @@
 // id; output in ascending block id with -1 padding.  Both kernels work on order-preserving
 // 32-bit keys and end with an in-order ballot pass that writes the chosen ids, which gives
 // ascending order and the lower-id tie rule for free.
-//   k_topk (many rows, or rows too long for registers): radix select; it skips the bits every
-//     candidate shares, then takes 8-bit digits from the top with an LDS histogram per pass,
-//     stopping as soon as the boundary digit's bucket is taken whole.
-//   k_topk_reg (few rows, decode): the row sits in registers and the k-th largest key is found
-//     by bisection with ballot counts.
+//   k_topk_reg (rows of up to 16384 blocks): the row sits in registers and the k-th largest key
+//     is found by bisection with ballot counts; the scores are read once.
+//   k_topk (longer rows): radix select; it skips the bits every candidate shares, then takes
+//     8-bit digits from the top with an LDS histogram per pass, stopping as soon as the boundary
+//     digit's bucket is taken whole.
 #include <type_traits>
 
 #include "msa_device.h"
@@ -157,8 +157,8 @@ __global__ __launch_bounds__(64 * NW) void k_topk(int B, int Hkv, int max_blocks
 // reads its R scores once, and the k-th largest key T is found bit by bit from the highest bit
 // the keys do not all share, counting the keys at or above each trial threshold with ballots.
 // T is the largest value with at least k keys >= T, so fewer than k keys are > T and the
-// boundary ties are taken in id order exactly as above.  Used when there are few rows (decode),
-// where the radix passes' round trips through memory and LDS dominate.
+// boundary ties are taken in id order exactly as above.  Against the radix passes it saves the
+// re-reads of the scores and the LDS histogram round trips.
 //
 // With page_table != NULL the same launch also writes the row's decode page table and row length
 // (as k_page_table below), from the chosen ids kept in LDS; the request lookup is issued at the
@@ -348,10 +348,6 @@ __global__ __launch_bounds__(256) void k_page_table(int rows, int B, int Hkv, in
   if (j == 0) row_len[rho] = len;
 }
 
-#ifndef MSA_TOPK_REG_MAX_ROWS
-#define MSA_TOPK_REG_MAX_ROWS 4096  // register top-k below this many rows, radix passes above
-#endif
-
 template <int NW, int R>
 static void launch_reg(int rows, hipStream_t stream, int Hkv, int max_blocks, const int32_t* q_pos,
                        const float* scores, int k, int32_t* sel, int32_t* cnt, const PageTableOut& pto) {
@@ -363,7 +359,7 @@ static void launch_reg(int rows, hipStream_t stream, int Hkv, int max_blocks, co
 // launched) when the shape needs the radix kernel, which does not build page tables.
 static bool launch_topk_reg(int rows, int Hkv, int max_blocks, const int32_t* q_pos, const float* scores, int k,
                             int32_t* sel, int32_t* cnt, const PageTableOut& pto, hipStream_t stream) {
-  if (rows >= MSA_TOPK_REG_MAX_ROWS || max_blocks > 16384) return false;
+  if (max_blocks > 16384) return false;
   // the smallest register layout that holds a row: 64*NW*R >= max_blocks
   auto go = [&](auto nw, auto r) {
     launch_reg<decltype(nw)::value, decltype(r)::value>(rows, stream, Hkv, max_blocks, q_pos, scores, k, sel, cnt,
@@ -387,10 +383,11 @@ hipError_t launch_topk(int B, int Nq, int Hkv, int max_blocks, const int32_t* cu
   const int rows = Nq * Hkv;
   const PageTableOut none{B, nullptr, nullptr, cu_q, nullptr, nullptr};
   if (launch_topk_reg(rows, Hkv, max_blocks, q_pos, scores, k, sel, cnt, none, stream)) return hipGetLastError();
-  if (rows < MSA_TOPK_REG_MAX_ROWS)  // few rows longer than the register layouts: 16 waves per row
+  // rows longer than the register layouts: radix passes, 16 waves per row when the rows are few
+  if (rows < 4096)
     hipLaunchKernelGGL(k_topk<16>, dim3(rows), dim3(1024), 0, stream, B, Hkv, max_blocks, cu_q, q_pos, scores, k,
                        sel, cnt);
-  else  // many rows: radix passes, one wave per row
+  else
     hipLaunchKernelGGL(k_topk<1>, dim3(rows), dim3(64), 0, stream, B, Hkv, max_blocks, cu_q, q_pos, scores, k, sel,
                        cnt);
   return hipGetLastError();

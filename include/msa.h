@@ -126,7 +126,7 @@ msa_status msa_build_sparse_page_table(const msa_batch* batch, int32_t num_kv_he
                                        int32_t* page_table, int32_t* row_len, msa_stream_t stream);
 
 /* msa_topk_blocks followed by msa_build_sparse_page_table, in one launch when the rows fit the
- * register top-k (fewer than 4096 rows of at most 16384 blocks; decode shapes), else in two.
+ * register top-k (max_blocks <= 16384), else in two.
  * Same arguments, outputs and results as the two calls; the fusion is the one the pages name as
  * open for MSA's small kernels (Chinese page, section "遗留问题"). */
 msa_status msa_topk_page_table(const msa_batch* batch, int32_t num_kv_heads, int32_t num_pages,

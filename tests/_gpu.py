@@ -21,10 +21,13 @@ def announce(*parts):
     sys.stdout.flush()
 
 
-def setup(wl: mi.Workload, on_gpu_generation: bool = False):
-    """(device inputs, cpu inputs or None).  Small cases are drawn on the CPU and copied."""
+def setup(wl: mi.Workload, on_gpu_generation: bool = False, host_copy: bool = False):
+    """(device inputs, cpu inputs or None).  Small cases are drawn on the CPU and copied; long ones can
+    be drawn on the GPU (CPU normal draws of hundreds of millions of values take minutes), with an
+    optional host copy of exactly those values for the oracle."""
     if on_gpu_generation:
-        return mi.make_inputs(wl, "cuda"), None
+        dev = mi.make_inputs(wl, "cuda")
+        return dev, (dev.to("cpu") if host_copy else None)
     cpu = mi.make_inputs(wl, "cpu")
     return cpu.to("cuda"), cpu
 

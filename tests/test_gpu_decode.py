@@ -33,9 +33,13 @@ CASES = {
     # one wave holding 4 and 8 scores per lane (up to 256 / 512 blocks)
     "topk_4_per_lane": dict(ctx=[30000, 700], nq=[1, 2], Hq=8, Hkv=2, D=64, Di=64, k=7),
     "topk_8_per_lane": dict(ctx=[60000, 33000], nq=[1, 1], Hq=8, Hkv=2, D=64, Di=64, k=64),
-    # >= 4096 rows: the radix-pass top-k
-    "many_rows_radix": dict(ctx=[3000] * 2 + [700] * 254, nq=[1] * 256, Hq=32, Hkv=16, D=64, Di=64, k=6),
+    # >= 4096 rows of short candidate lists
+    "many_rows": dict(ctx=[3000] * 2 + [700] * 254, nq=[1] * 256, Hq=32, Hkv=16, D=64, Di=64, k=6),
+    # rows beyond the register layouts (> 16384 blocks): the radix-pass top-k, 16 waves per row,
+    # and the two-launch form of msa_topk_page_table
+    "topk_radix_long_rows": dict(ctx=[2100000], nq=[1], Hq=4, Hkv=1, D=64, Di=64, k=9),
 }
+GPU_DRAWN = {"topk_16_waves", "topk_radix_long_rows"}   # inputs drawn on the GPU, copied to the host
 
 
 def _wl(name, seed=21):
@@ -59,7 +63,7 @@ def _run(dev, max_q=None):
 @pytest.mark.parametrize("name", list(CASES))
 def test_decode_path_matches_oracle(name):
     announce("decode", name)
-    dev, cpu = setup(_wl(name))
+    dev, cpu = setup(_wl(name), on_gpu_generation=name in GPU_DRAWN, host_copy=True)
     x = np_inputs(cpu)
     wl = dev.wl
     s, sel, cnt, pt, rl, out, lse = [host(t) for t in _run(dev)]
