@@ -289,10 +289,14 @@ __global__ __launch_bounds__(256) void k_merge_splits(int parts, int G, const fl
   }
 }
 
-// One wavefront per row.  The row's parts*G log-sum-exps go to LDS and become normalized
-// weights w[j][h] = exp(lse_j - LSE) once; then every lane accumulates its 8-element chunks over
-// the parts with independent 16-byte loads (absent parts have weight 0 and are not read).
+// One wavefront per row.  Lanes 0..G-1 turn the row's parts*G log-sum-exps into normalized
+// weights w[j][h] = exp(lse_j - LSE) in LDS (0 for absent parts) and note each head's first
+// present part.  Then every lane combines its 8-element chunks (up to four per lane) over the
+// parts in batches of eight, all of a batch's 16-byte loads issued together and streamed past
+// the caches.  An absent part is read from the head's first present part instead (finite values,
+// weight 0), so no load depends on a branch.
 constexpr int kMergeMaxPG = 64 * 16;  // parts * G
+constexpr int kMergeBatch = 8;
 
 template <typename TIn>
 __global__ __launch_bounds__(256) void k_lse_merge(int64_t rows, int parts, int G, int D,
@@ -300,67 +304,75 @@ __global__ __launch_bounds__(256) void k_lse_merge(int64_t rows, int parts, int 
                                                    bf16* __restrict__ out, float* __restrict__ lse_out) {
   __shared__ float s_w[4][kMergeMaxPG];
   __shared__ float s_lse[4][16];
-  __shared__ int s_parts[4][64];
+  __shared__ int s_first[4][16];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * 4 + wv;
   if (row >= rows) return;
-  const int PG = parts * G, GD = G * D;
+  const int PG = parts * G, GD = G * D, NCH = GD / 8;
   float* w = s_w[wv];
   const float* pl = part_lse + row * PG;
-  for (int i = lane; i < PG; i += kWave) w[i] = pl[i];
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  if (lane < G) {  // per head: LSE and the normalization
+  if (lane < G) {  // per head: LSE, the normalized weights and the first present part
     float M = neg_inf();
-    for (int j = 0; j < parts; ++j) M = fmaxf(M, w[j * G + lane]);
+    int first = -1;
+    for (int j = 0; j < parts; ++j) {
+      const float lj = pl[j * G + lane];
+      M = fmaxf(M, lj);
+      if (first < 0 && lj != neg_inf()) first = j;
+    }
     float den = 0.f;
     for (int j = 0; j < parts; ++j) {
-      const float lj = w[j * G + lane];
+      const float lj = pl[j * G + lane];
       den += lj == neg_inf() ? 0.f : __expf(lj - M);
     }
     const float inv = 1.f / den;
     for (int j = 0; j < parts; ++j) {
-      const float lj = w[j * G + lane];
+      const float lj = pl[j * G + lane];
       w[j * G + lane] = lj == neg_inf() ? 0.f : __expf(lj - M) * inv;
     }
     s_lse[wv][lane] = M + __logf(den);
+    s_first[wv][lane] = first;
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  // compact list of the parts present for at least one head (lane j tests part j; parts <= 64)
-  bool present = false;
-  if (lane < parts)
-    for (int h = 0; h < G; ++h) present = present || (pl[lane * G + h] != neg_inf());
-  const uint64_t pm = __ballot(present);
-  if (present) s_parts[wv][__popcll(pm & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))))] = lane;
-  const int np = __popcll(pm);
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  const int* plist = s_parts[wv];
-  for (int c = lane; c < GD / 8; c += kWave) {
+  const TIn* src = part_o + (row * parts) * (int64_t)GD;
+  for (int c = lane; c < NCH; c += kWave) {
     const int h = (8 * c) / D;
+    const int jp = s_first[wv][h];
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const TIn* src = part_o + (row * parts) * (int64_t)GD + 8 * c;
-#pragma unroll 4
-    for (int q = 0; q < np; ++q) {
-      const int j = plist[q];
-      const float wj = w[j * G + h];
-      const bool use = wj != 0.f;  // a part absent for this head only: its values are never used
+    for (int jb = 0; jb < parts; jb += kMergeBatch) {
+      float wj[kMergeBatch];
+      int jj[kMergeBatch];
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const int j = jb + u;
+        wj[u] = j < parts ? w[j * G + h] : 0.f;
+        jj[u] = (j < parts && wj[u] != 0.f) ? j : jp;
+      }
       if constexpr (sizeof(TIn) == 2) {
-        const u32x4 v = ld16(src + (int64_t)j * GD);
+        u32x4 v[kMergeBatch];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += use ? wj * __uint_as_float(v[e] << 16) : 0.f;
-          acc[2 * e + 1] += use ? wj * __uint_as_float(v[e] & 0xffff0000u) : 0.f;
-        }
+        for (int u = 0; u < kMergeBatch; ++u) v[u] = ld16_nt(src + (int64_t)jj[u] * GD + 8 * c);
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += wj[u] * __uint_as_float(v[u][e] << 16);
+            acc[2 * e + 1] += wj[u] * __uint_as_float(v[u][e] & 0xffff0000u);
+          }
       } else {
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(src + (int64_t)j * GD);
-        const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + (int64_t)j * GD + 4);
+        f32x4 v0[kMergeBatch], v1[kMergeBatch];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[e] += use ? wj * v0[e] : 0.f;
-          acc[4 + e] += use ? wj * v1[e] : 0.f;
+        for (int u = 0; u < kMergeBatch; ++u) {
+          v0[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)jj[u] * GD + 8 * c);
+          v1[u] = *reinterpret_cast<const f32x4*>(src + (int64_t)jj[u] * GD + 8 * c + 4);
         }
+#pragma unroll
+        for (int u = 0; u < kMergeBatch; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[e] += wj[u] * v0[u][e];
+            acc[4 + e] += wj[u] * v1[u][e];
+          }
       }
     }
     u32x4 o;

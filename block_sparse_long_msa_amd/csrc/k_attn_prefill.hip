@@ -29,8 +29,19 @@
 
 namespace msa {
 
-constexpr int kChunk = 256;  // query tokens per work item
-constexpr int kNT = 2;       // 16-row MFMA N tiles per wave per pass
+#ifndef MSA_KVBM_WAVES
+#define MSA_KVBM_WAVES 4
+#endif
+#ifndef MSA_KVBM_NT
+#define MSA_KVBM_NT 2
+#endif
+#ifndef MSA_KVBM_OCC
+#define MSA_KVBM_OCC 2
+#endif
+constexpr int kChunk = 256;               // query tokens per work item
+constexpr int kNT = MSA_KVBM_NT;          // 16-row MFMA N tiles per wave per pass
+constexpr int kWaves = MSA_KVBM_WAVES;    // waves per workgroup, sharing one staged block
+constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;     // MI355X: workgroups are dealt round-robin to 8 XCDs
 constexpr float kLog2eP = 1.4426950408889634f;
 constexpr float kLn2P = 0.6931471805599453f;
@@ -165,7 +176,7 @@ __device__ __forceinline__ int vt_swz(int d, int tok) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_attn_kvbm(
+__global__ __launch_bounds__(kThreads, MSA_KVBM_OCC) void k_attn_kvbm(
     int B, int Hkv, int G, int k, int max_blocks, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q,
     const bf16* __restrict__ kcache, const bf16* __restrict__ vcache, const int32_t* __restrict__ offsets,
@@ -208,27 +219,28 @@ __global__ __launch_bounds__(256, 2) void k_attn_kvbm(
   const bf16* kg = kcache + ((int64_t)page * kBlock * Hkv + g) * D;
   const bf16* vg = vcache + ((int64_t)page * kBlock * Hkv + g) * D;
   const int tstride = Hkv * D;
-  constexpr int NKL = kBlock * D / 8 / 256, NVL = kBlock * D / 16 / 256;
+  static_assert(kBlock * D / 16 % kThreads == 0, "staging assumes whole rounds of 16-byte loads");
+  constexpr int NKL = kBlock * D / 8 / kThreads, NVL = kBlock * D / 16 / kThreads;
   u32x4 kst[NKL], vst[NVL][2];
 #pragma unroll
   for (int c = 0; c < NKL; ++c) {
-    const int idx = tid + 256 * c, tok = min(idx / (D / 8), in_block - 1), ch = idx % (D / 8);
+    const int idx = tid + kThreads * c, tok = min(idx / (D / 8), in_block - 1), ch = idx % (D / 8);
     kst[c] = ld16(kg + tok * tstride + ch * 8);
   }
 #pragma unroll
   for (int c = 0; c < NVL; ++c) {
-    const int idx = tid + 256 * c, tp = idx % (kBlock / 2), ch = idx / (kBlock / 2);
+    const int idx = tid + kThreads * c, tp = idx % (kBlock / 2), ch = idx / (kBlock / 2);
     vst[c][0] = ld16(vg + min(2 * tp, in_block - 1) * tstride + ch * 8);
     vst[c][1] = ld16(vg + min(2 * tp + 1, in_block - 1) * tstride + ch * 8);
   }
 #pragma unroll
   for (int c = 0; c < NKL; ++c) {
-    const int idx = tid + 256 * c, tok = idx / (D / 8), ch = idx % (D / 8);
+    const int idx = tid + kThreads * c, tok = idx / (D / 8), ch = idx % (D / 8);
     st16(&k_lds[tok * KST + ch * 8], kst[c]);
   }
 #pragma unroll
   for (int c = 0; c < NVL; ++c) {  // two tokens per lane -> 32-bit transposed writes
-    const int idx = tid + 256 * c, tp = idx % (kBlock / 2), ch = idx / (kBlock / 2);
+    const int idx = tid + kThreads * c, tp = idx % (kBlock / 2), ch = idx / (kBlock / 2);
     const int t0 = 2 * tp;
     const u32x4 a = vst[c][0], bb = vst[c][1];
 #pragma unroll
@@ -248,7 +260,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_kvbm(
   const int n_e = e_end - e_begin;             // query tokens of this work item
 
   // the item's (t, j) entries and query positions, once, in LDS
-  for (int i = tid; i < n_e; i += 256) {
+  for (int i = tid; i < n_e; i += kThreads) {
     const int packed = entries[e_begin + i];
     s_tj[i] = packed;
     s_pos[i] = q_pos[packed >> 6];
@@ -266,21 +278,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_kvbm(
       const int rr = 16 * nt + n, sl = rr / G, h = rr % G;
       const int li = lb + sl;
       const bool ok = li < n_e;
-      const int packed = ok ? s_tj[li] : 0;
+      // a row past the chunk end reads the chunk's last query row (finite values) and gets
+      // position -1, so every key is masked for it and it is never stored
+      const int packed = s_tj[min(li, n_e - 1)];
       P.tj[nt] = ok ? packed : -1;
       P.pos[nt] = ok ? s_pos[li] : -1;
       const bf16* qrow = q + ((int64_t)(packed >> 6) * Hq + g * G + h) * D + 8 * qd;
-      const uint32_t msk = ok ? 0xffffffffu : 0u;
 #pragma unroll
-      for (int kw = 0; kw < KW; ++kw) P.qf[nt][kw] = ld16(qrow + 32 * kw) & msk;
+      for (int kw = 0; kw < KW; ++kw) P.qf[nt][kw] = ld16(qrow + 32 * kw);
     }
   };
   PassQ nxt;
   if (w * tpw < n_e) load_pass(nxt, w * tpw);
 
-  for (int lb = w * tpw; lb < n_e; lb += 4 * tpw) {
+  for (int lb = w * tpw; lb < n_e; lb += kWaves * tpw) {
     const PassQ cur = nxt;
-    if (lb + 4 * tpw < n_e) load_pass(nxt, lb + 4 * tpw);
+    if (lb + kWaves * tpw < n_e) load_pass(nxt, lb + kWaves * tpw);
     const auto& qf = cur.qf;
     const int* pos = cur.pos;
     const int* tj = cur.tj;
@@ -333,8 +346,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_kvbm(
     for (int nt = 0; nt < kNT; ++nt) {
       float m = neg_inf();
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-        m = fmaxf(fmaxf(m, fmaxf(sacc[nt][mt][0], sacc[nt][mt][1])), fmaxf(sacc[nt][mt][2], sacc[nt][mt][3]));
+      for (int mt = 0; mt < 8; mt += 2)
+        m = fmaxf(m, fmaxf(fmaxf(fmaxf(sacc[nt][mt][0], sacc[nt][mt][1]), fmaxf(sacc[nt][mt][2], sacc[nt][mt][3])),
+                           fmaxf(fmaxf(sacc[nt][mt + 1][0], sacc[nt][mt + 1][1]),
+                                 fmaxf(sacc[nt][mt + 1][2], sacc[nt][mt + 1][3]))));
       m = max_over_quads(m);
       const float mb = (m == neg_inf()) ? 0.f : m * scale_log2;
       float l = 0.f;
@@ -347,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_kvbm(
           l += p;
         }
       mrow[nt] = mb;
-      lrow[nt] = sum_over_quads(l);
+      lrow[nt] = sum_over_quads(l);  // fp32 sum: the LSE keeps fp32 accuracy
     }
     // P (bf16) as the B operand of the PV MFMA, in the S tile's own token order
     u32x4 pb[kNT][KS];
@@ -371,7 +386,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_kvbm(
       const int rr = 16 * nt + n, h = rr % G;
       const int t = tj[nt] >> 6, j = tj[nt] & 63;
       orow[nt] = (((int64_t)t * Hkv + g) * k + j) * G + h;
-      inv[nt] = 1.f / lrow[nt];
+      inv[nt] = __builtin_amdgcn_rcpf(lrow[nt]);
       if (tj[nt] >= 0 && qd == 0) part_lse[orow[nt]] = (mrow[nt] + fast_log2(lrow[nt])) * kLn2P;
     }
     // O^T = V^T P^T, one pair of 16-row d tiles at a time.  Tile rows are permuted so that lane
@@ -438,11 +453,11 @@ hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blo
   const bf16* vc = static_cast<const bf16*>(vcache);
   bf16* po = static_cast<bf16*>(part_o);
   if (D == 128)
-    hipLaunchKernelGGL(k_attn_kvbm<128>, dim3(grid), dim3(256), 0, stream, B, Hkv, G, k, max_blocks, block_table,
+    hipLaunchKernelGGL(k_attn_kvbm<128>, dim3(grid), dim3(kThreads), 0, stream, B, Hkv, G, k, max_blocks, block_table,
                        ctx_len, q_pos, qq, kc, vc, ws.offsets, ws.item_off, ws.items, ws.entries, NB, sl2, po,
                        part_lse);
   else
-    hipLaunchKernelGGL(k_attn_kvbm<64>, dim3(grid), dim3(256), 0, stream, B, Hkv, G, k, max_blocks, block_table,
+    hipLaunchKernelGGL(k_attn_kvbm<64>, dim3(grid), dim3(kThreads), 0, stream, B, Hkv, G, k, max_blocks, block_table,
                        ctx_len, q_pos, qq, kc, vc, ws.offsets, ws.item_off, ws.items, ws.entries, NB, sl2, po,
                        part_lse);
   return hipGetLastError();

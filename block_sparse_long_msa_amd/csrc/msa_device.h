@@ -53,14 +53,32 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 
-// Reduce across the four 16-lane groups (lanes l, l^16, l^32, l^48).
+// Reduce across the four 16-lane groups (lanes l, l^16, l^32, l^48) with gfx950's lane-swap
+// instructions, which are VALU ops with no LDS round trip.  v_permlane32_swap on two copies of v
+// leaves one holding the lower 32 lanes twice and the other the upper 32 lanes twice, so
+// combining the two pairs every lane l with l^32; v_permlane16_swap does the same for l^16.
+// Every lane ends with the same value, combined in the same order.
+__device__ __forceinline__ void swap32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float max_over_quads(float v) {
-  v = fmaxf(v, shfl_xor(v, 16));
-  return fmaxf(v, shfl_xor(v, 32));
+  float a, b;
+  swap32(v, a, b);
+  swap16(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float sum_over_quads(float v) {
-  v += shfl_xor(v, 16);
-  return v + shfl_xor(v, 32);
+  float a, b;
+  swap32(v, a, b);
+  swap16(a + b, a, b);
+  return a + b;
 }
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
