@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--fused-topk", action="store_true",
                    help="prefill: score and select with the fused msa_index_topk instead of two calls")
+    p.add_argument("--prefill-mode", default="kvbm", choices=["kvbm", "query-major"],
+                   help="prefill attention: KV-block-major with LSE merge (the method), or the query-major "
+                        "baseline it is measured against (each row reads its own blocks)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, run one plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -182,7 +185,7 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import block_sparse_long_msa_amd as msa
-    from block_sparse_long_msa_amd.pipeline import MSADecode, MSAPrefill
+    from block_sparse_long_msa_amd.pipeline import MSADecode, MSAPrefill, MSAPrefillQueryMajor
     msa.load()
     torch.cuda.set_device(0)
 
@@ -194,8 +197,11 @@ def main():
     gen_s = time.time() - t0
     b = msa.Batch(dev.block_table, dev.ctx_len, dev.cu_q, dev.q_pos, max(wl.q_counts))
     P = dev.kcache.shape[0]
+    query_major = not decode and args.prefill_mode == "query-major"
     if decode:
         run = MSADecode(b, wl.Hkv, wl.G, wl.D, wl.k, P)
+    elif query_major:
+        run = MSAPrefillQueryMajor(b, wl.Hkv, wl.G, wl.D, wl.k, P)
     else:
         run = MSAPrefill(b, wl.Hkv, wl.G, wl.D, wl.k, P, fused=args.fused_topk)
     flush = None
@@ -207,7 +213,7 @@ def main():
         flush.sum()
 
     # stage boundaries for per-kernel event timing
-    stages = ["score", "select", "attend"] + ([] if decode else ["merge"])
+    stages = ["score", "select", "attend"] + ([] if decode or query_major else ["merge"])
 
     def step(evs=None):
         for i, name in enumerate(stages):
@@ -273,10 +279,19 @@ def main():
                 "achieved": score_flops / (score_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "traffic": None, "algorithmic_flops": score_flops, "avg_ms": score_ms}
         attn_flops = 4.0 * sel_tok * wl.G * wl.D               # QK^T and PV over the selected tokens
-        roof_attn = {"kernel": "msa_sparse_attn_prefill", "bound": "mfma",
-                     "achieved": attn_flops / (attend_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "algorithmic_flops": attn_flops, "avg_ms": attend_ms}
-    for r in (roof, roof_attn):
+        roof_attn = {"kernel": "k_attn_decode (query-major rows)" if query_major else "msa_sparse_attn_prefill",
+                     "bound": "mfma", "achieved": attn_flops / (attend_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "algorithmic_flops": attn_flops, "avg_ms": attend_ms,
+                     # K/V bytes the attention mapping moves from memory: query-major reads every
+                     # selected block once per (token, KV head) row, KV-block-major once per work item
+                     "kv_bytes_moved": sel_tok * wl.D * 2 * 2 if query_major else None}
+    details = [roof, roof_attn]
+    if not decode and not query_major:
+        merge_ms = float(per_stage[:, 3].mean())
+        merge_bytes = (run.part_o.numel() * 2 + run.part_lse.numel() * 4 + run.out.numel() * 2 + run.lse.numel() * 4)
+        details.append({"kernel": "k_lse_merge<bf16>", "bound": "hbm", "achieved": merge_bytes / (merge_ms * 1e-3) / 1e9,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "algorithmic_bytes": merge_bytes, "avg_ms": merge_ms})
+    for r in details:
         r["frac"] = r["achieved"] / r["peak"]
 
     cpu = None
@@ -291,9 +306,10 @@ def main():
                    "query_tokens": wl.Nq, "ctx_len": wl.ctx_lens[0] if len(set(wl.ctx_lens)) == 1 else "ragged",
                    "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "Di": wl.Di, "top_k": wl.k, "block": wl.block,
                    "l2_flush_between_steps": flush is not None,
-                   "fused_index_topk": bool(args.fused_topk and not decode)},
+                   "fused_index_topk": bool(args.fused_topk and not decode),
+                   "prefill_mode": None if decode else args.prefill_mode},
         "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
-        "roofline_detail": [roof, roof_attn],
+        "roofline_detail": details,
         "stage_ms": {name: float(per_stage[:, i].mean()) for i, name in enumerate(stages)},
         "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
         "cpu_baseline": cpu,

@@ -130,8 +130,8 @@ def msa_sparse_attn_decode(rows: int, G: int, D: int, q, k_base, v_base, page_st
                                         _ptr(page_table, torch.int32, "page_table"), k,
                                         _ptr(row_len, torch.int32, "row_len"), sm_scale,
                                         _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse", True),
-                                        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
-                                        _stream(stream)))
+                                        _ptr(workspace, torch.uint8, "workspace", True),
+                                        0 if workspace is None else workspace.numel(), _stream(stream)))
 
 
 def msa_sparse_attn_prefill_workspace_size(batch: Batch, num_kv_heads: int, k: int) -> int:

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
   constexpr int OST = D + 4;  // padded LDS row of the per-wave outputs
   __shared__ float sm_m[4][16], sm_l[4][16];
   __shared__ __align__(16) float sm_o[4][16][OST];
-  const int sp = blockIdx.x, rho = blockIdx.y;
+  const int sp = (int)(blockIdx.x % (unsigned)nsplit), rho = (int)(blockIdx.x / (unsigned)nsplit);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, qd = lane >> 4;
   const int j0 = sp * ppw;
   const int32_t* pt = page_table + (int64_t)rho * k;
@@ -395,7 +395,7 @@ hipError_t launch_attn_decode(int rows, int G, int D, const void* q, const void*
                               float* ws_lse, hipStream_t stream) {
   const int nsplit = decode_splits(rows, k);
   const int ppw = (k + nsplit - 1) / nsplit;
-  dim3 grid(nsplit, rows), block(256);
+  dim3 grid((unsigned)((int64_t)nsplit * rows)), block(256);
   const float sl2 = sm_scale * kLog2e;
   const bf16* qq = static_cast<const bf16*>(q);
   const bf16* kk = static_cast<const bf16*>(kview);

@@ -29,6 +29,7 @@ hipError_t launch_topk_page_table(int B, int Nq, int Hkv, int max_blocks, const 
                                   const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos,
                                   const float* scores, int k, int32_t* sel, int32_t* cnt, int32_t* page_table,
                                   int32_t* row_len, hipStream_t stream);
+int decode_splits(int rows, int k);
 hipError_t launch_attn_decode(int rows, int G, int D, const void* q, const void* kview, const void* vview,
                               int64_t page_stride, int64_t token_stride, const int32_t* page_table, int k,
                               const int32_t* row_len, float sm_scale, void* out, float* lse, float* ws_o,
@@ -250,7 +251,9 @@ msa_status msa_topk_page_table(const msa_batch* batch, int32_t num_kv_heads, int
 
 size_t msa_sparse_attn_decode_workspace_size(int32_t rows, int32_t G, int32_t D, int32_t k) {
   if (rows <= 0 || G <= 0 || D <= 0 || k <= 0) return 0;
-  const size_t parts = (size_t)rows * k * G;
+  const int nsplit = msa::decode_splits(rows, k);
+  if (nsplit == 1) return 0;  // each row in one workgroup: outputs are written directly
+  const size_t parts = (size_t)rows * nsplit * G;
   return align256(parts * D * sizeof(float)) + align256(parts * sizeof(float));
 }
 
@@ -267,20 +270,21 @@ msa_status msa_sparse_attn_decode(int32_t rows, int32_t G, int32_t D, const void
   MSA_REQUIRE(page_stride > 0 && token_stride > 0 && page_stride % 8 == 0 && token_stride % 8 == 0,
               MSA_ERR_INVALID_ARG, "page_stride and token_stride must be positive multiples of 8 elements");
   if (rows == 0) return MSA_OK;
-  MSA_REQUIRE(q && k_base && v_base && page_table && row_len && out && workspace, MSA_ERR_INVALID_ARG,
-              "q, k_base, v_base, page_table, row_len, out and workspace must be non-NULL");
+  MSA_REQUIRE(q && k_base && v_base && page_table && row_len && out, MSA_ERR_INVALID_ARG,
+              "q, k_base, v_base, page_table, row_len and out must be non-NULL");
   MSA_REQUIRE(aligned16(q) && aligned16(k_base) && aligned16(v_base) && aligned16(out) && aligned16(workspace),
               MSA_ERR_INVALID_ARG, "q, k_base, v_base, out and workspace must be 16-byte aligned");
   MSA_REQUIRE(aligned4(page_table) && aligned4(row_len) && aligned4(lse), MSA_ERR_INVALID_ARG,
               "page_table, row_len and lse must be 4-byte aligned");
-  MSA_REQUIRE(rows <= kMaxGridY, MSA_ERR_UNSUPPORTED, "rows must be <= %d", kMaxGridY);
+  MSA_REQUIRE((int64_t)rows * k <= 0x7fffffffLL, MSA_ERR_UNSUPPORTED, "rows*k must fit in int32");
   MSA_REQUIRE(token_stride * 128 + D <= 0x7fffffffLL, MSA_ERR_UNSUPPORTED, "token_stride*128 must fit in int32");
   const size_t need = msa_sparse_attn_decode_workspace_size(rows, G, D, k);
-  MSA_REQUIRE(workspace_bytes >= need, MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
-              workspace_bytes);
-  const size_t parts = (size_t)rows * k * G;
+  MSA_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), MSA_ERR_WORKSPACE_TOO_SMALL,
+              "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  const size_t parts = (size_t)rows * msa::decode_splits(rows, k) * G;
   float* ws_o = static_cast<float*>(workspace);
-  float* ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(parts * D * sizeof(float)));
+  float* ws_lse = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(parts * D * sizeof(float)))
+                       : nullptr;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return from_hip(msa::launch_attn_decode(rows, G, D, q, k_base, v_base, page_stride, token_stride, page_table, k,
                                           row_len, sm_scale, out, lse, ws_o, ws_lse, st),

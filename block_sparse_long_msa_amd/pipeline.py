@@ -3,6 +3,9 @@
 MSADecode: index scores -> top-k + sparse page table -> decode attention (split over pages,
            merged in the library).
 MSAPrefill: index scores -> top-k -> KV-block-major attention (partials) -> LSE merge.
+MSAPrefillQueryMajor: the query-major baseline the KV-block-major mapping is measured against:
+           index scores -> top-k + page table -> every (query token, KV head) row attends to its own
+           k blocks with the paged decode kernel (no partials, no merge, K/V re-read per row).
 
 Buffers are allocated once with torch (device memory only); every step runs in libmsa.so.
 """
@@ -104,4 +107,41 @@ class MSAPrefill:
         self.select(stream)
         self.attend(q, kcache, vcache, sm_scale, stream)
         self.merge(stream)
+        return self.out, self.lse
+
+
+class MSAPrefillQueryMajor:
+    """Prefill attention query-major, for A/B against ``MSAPrefill``: the selection is turned into a
+    per-row page table (ascending blocks, so only the diagonal block is partial) and each row reads
+    its k blocks itself.  Same outputs as ``MSAPrefill`` up to rounding (bf16 partials there)."""
+
+    def __init__(self, batch: Batch, Hkv: int, G: int, D: int, k: int, num_pages: int, device="cuda"):
+        Nq, mb = batch.num_queries, batch.max_blocks
+        self.batch, self.Hkv, self.G, self.D, self.k, self.num_pages = batch, Hkv, G, D, k, num_pages
+        self.rows = Nq * Hkv
+        self.scores = torch.empty((Nq, Hkv, mb), dtype=torch.float32, device=device)
+        self.sel = torch.empty((Nq, Hkv, k), dtype=torch.int32, device=device)
+        self.cnt = torch.empty((Nq, Hkv), dtype=torch.int32, device=device)
+        self.page_table = torch.empty((self.rows, k), dtype=torch.int32, device=device)
+        self.row_len = torch.empty((self.rows,), dtype=torch.int32, device=device)
+        self.out = torch.empty((Nq, Hkv * G, D), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((Nq, Hkv * G), dtype=torch.float32, device=device)
+        ws = msa_sparse_attn_decode_workspace_size(self.rows, G, D, k)
+        self.ws = torch.empty((ws,), dtype=torch.uint8, device=device) if ws else None
+
+    def score(self, q_idx, kidx, stream=None):
+        msa_index_score(self.batch, q_idx, kidx, self.scores, stream)
+
+    def select(self, stream=None):
+        msa_topk_page_table(self.batch, self.Hkv, self.num_pages, self.scores, self.k, self.sel, self.cnt,
+                            self.page_table, self.row_len, stream)
+
+    def attend(self, q, kcache, vcache, sm_scale: float, stream=None):
+        msa_sparse_attn_decode(self.rows, self.G, self.D, q, kcache, vcache, self.D, self.Hkv * self.D,
+                               self.page_table, self.k, self.row_len, sm_scale, self.out, self.lse, self.ws, stream)
+
+    def __call__(self, q, q_idx, kcache, vcache, kidx, sm_scale: float, stream=None):
+        self.score(q_idx, kidx, stream)
+        self.select(stream)
+        self.attend(q, kcache, vcache, sm_scale, stream)
         return self.out, self.lse

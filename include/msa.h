@@ -137,13 +137,17 @@ msa_status msa_topk_page_table(const msa_batch* batch, int32_t num_kv_heads, int
  * G query heads q[rho*G .. rho*G+G-1] to the first row_len[rho] tokens of its virtual pages.
  * Token i of row rho is virtual page v = page_table[rho, i/128], slot s = i%128, and its
  * element d is at k_base[v*page_stride + s*token_stride + d] (same for v_base).
- * Softmax scale sm_scale, natural-log LSE.  Work is split over the row's pages and combined
- * by a log-sum-exp merge through the workspace.
+ * Softmax scale sm_scale, natural-log LSE.  When there are too few rows to fill the GPU, each
+ * row's pages are split over several workgroups and the parts combined by a log-sum-exp merge
+ * through the workspace; otherwise no workspace is used (size 0, pointer may be NULL).
+ * Only a row's last page may be partial, which holds for selections in ascending block order, so
+ * the same call also runs prefill rows query-major (rows = Nq*Hkv, one query token per row,
+ * page table from msa_topk_page_table): each row reads its own k blocks, with no partials.
  *   q        device bf16 [rows*G, D]  (= [Nq, Hq, D] when rows = Nq*Hkv)
  *   out      device bf16 [rows*G, D]
  *   lse      device f32 [rows*G] or NULL
  *   workspace  device, >= msa_sparse_attn_decode_workspace_size(rows, G, D, k) bytes
- * Rows with row_len = 0 are invalid input. */
+ * Rows with row_len = 0 are invalid input; rows*k must fit in int32. */
 msa_status msa_sparse_attn_decode(int32_t rows, int32_t G, int32_t D, const void* q, const void* k_base,
                                   const void* v_base, int64_t page_stride, int64_t token_stride,
                                   const int32_t* page_table, int32_t k, const int32_t* row_len,

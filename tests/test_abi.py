@@ -116,7 +116,7 @@ def test_topk_page_table_rejects_null_outputs(lib):
     (8, 96, 96, 768, 16, 1 << 30, UNSUPPORTED),
     (8, 128, 100, 1024, 16, 1 << 30, INVALID),      # page stride not a multiple of 8 elements
     (8, 128, 128, 1024, 0, 1 << 30, UNSUPPORTED),
-    (8, 128, 128, 1024, 16, 64, WS_SMALL),
+    (8, 128, 128, 1024, 16, 64, WS_SMALL),             # 4 rows are split: a workspace is needed
     (8, 128, 128, 1 << 24, 16, 1 << 30, UNSUPPORTED),   # token_stride*128 beyond int32
 ])
 def test_decode_attention_rejects(lib, G, D, ps, ts, k, ws, status):
@@ -154,7 +154,10 @@ def test_empty_inputs_launch_nothing(lib):
 
 
 def test_workspace_sizes(lib):
-    assert lib.msa_sparse_attn_decode_workspace_size(64, 8, 128, 16) >= 64 * 16 * 8 * 129 * 4
+    # few rows: split over page runs (here 4 runs of 4 pages), fp32 partials + LSE per run
+    assert lib.msa_sparse_attn_decode_workspace_size(64, 8, 128, 16) >= 64 * 4 * 8 * 129 * 4
+    # enough rows to fill the GPU one workgroup each: no workspace
+    assert lib.msa_sparse_attn_decode_workspace_size(4096, 8, 128, 16) == 0
     assert lib.msa_sparse_attn_decode_workspace_size(0, 8, 128, 16) == 0
     b = _batch(B=1, Nq=32768, max_blocks=1024, maxq=32768)
     assert lib.msa_sparse_attn_prefill_workspace_size(ctypes.byref(b), 8, 16) >= 32768 * 8 * 16 * 4

@@ -165,6 +165,17 @@ def test_long_prefill_full():
                                            cnt[rows], wl.block, dev.scale)
     assert_attn_close(out[rows], ref_o, what="sampled merged output")
     assert np.abs(lse[rows] - ref_l).max() <= 1e-3
+    # the query-major baseline selects the same blocks and gives the same attention on them
+    from block_sparse_long_msa_amd.pipeline import MSAPrefillQueryMajor
+    qm = MSAPrefillQueryMajor(b, wl.Hkv, wl.G, wl.D, wl.k, dev.kcache.shape[0])
+    qm.out.fill_(float("nan"))
+    qm(dev.q, dev.q_idx, dev.kcache, dev.vcache, dev.kidx, dev.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(qm.sel), sel) and np.array_equal(host(qm.cnt), cnt)
+    qo, ql = host(qm.out), host(qm.lse)
+    assert np.all(np.isfinite(qo)) and np.all(np.isfinite(ql))
+    assert_attn_close(qo[rows], ref_o, what="sampled query-major output")
+    assert np.abs(ql[rows] - ref_l).max() <= 1e-3
 
 
 def test_tiny_prefill_full():

@@ -10,7 +10,7 @@ import pytest
 
 import msa_inputs as mi
 import oracle
-from _gpu import announce, batch, host, prefill, scores, setup, topk
+from _gpu import announce, batch, decode_attention, host, prefill, scores, setup, topk, topk_page_table
 from _helpers import assert_attn_close, np_inputs, selection_excused
 
 pytestmark = pytest.mark.gpu
@@ -79,3 +79,24 @@ def test_prefill_is_deterministic():
     b = [host(t) for t in _run(dev)]
     for u, v in zip(a, b):
         assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_query_major_matches_oracle(name):
+    """The query-major baseline (every (token, KV head) row reads its own k blocks through the
+    paged decode kernel) gives the oracle's attention on the same selection, without partials."""
+    announce("prefill query-major", name)
+    dev, cpu = setup(_wl(name))
+    x = np_inputs(cpu)
+    wl = dev.wl
+    b = batch(dev)
+    s = scores(dev, b)
+    sel, cnt, pt, rl = topk_page_table(dev, b, s)
+    out, lse = decode_attention(dev, pt, rl)
+    sel, cnt, out, lse = host(sel), host(cnt), host(out), host(lse)
+    o_pt, o_rl = oracle.sparse_page_table(sel, cnt, x.block_table, x.ctx_len, x.q_req, x.q_pos, wl.Hkv, wl.block)
+    assert np.array_equal(host(pt), o_pt) and np.array_equal(host(rl), o_rl)
+    ref_o, ref_l = oracle.sparse_attention(x.q, x.kcache, x.vcache, x.block_table, x.ctx_len, x.q_req, x.q_pos,
+                                           sel, cnt, wl.block, x.scale)
+    assert_attn_close(out, ref_o, what="query-major output")
+    assert np.abs(lse - ref_l).max() <= 1e-3
