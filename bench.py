@@ -29,6 +29,7 @@ import msa_inputs as mi  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+HOST_LINK_PEAK_GBS = 64.0      # PCIe Gen5 x16, one direction, GB/s (K/V read from host memory)
 METRIC = "MSA prefill/decode tokens/s; scorer HBM GB/s and attn MFMA % of peak, 1 GPU"
 
 
@@ -47,6 +48,9 @@ def parse():
     p.add_argument("--prefill-mode", default="kvbm", choices=["kvbm", "query-major"],
                    help="prefill attention: KV-block-major with LSE merge (the method), or the query-major "
                         "baseline it is measured against (each row reads its own blocks)")
+    p.add_argument("--kv-on-host", action="store_true",
+                   help="decode: keep the key-index cache in HBM but move the K/V caches to pinned host memory; "
+                        "attention then reads only the selected blocks over the host link")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, run one plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -198,6 +202,11 @@ def main():
     b = msa.Batch(dev.block_table, dev.ctx_len, dev.cu_q, dev.q_pos, max(wl.q_counts))
     P = dev.kcache.shape[0]
     query_major = not decode and args.prefill_mode == "query-major"
+    kv_on_host = decode and args.kv_on_host
+    kv_k, kv_v = dev.kcache, dev.vcache
+    if kv_on_host:      # pinned host copies; the kernels read them in place over the host link
+        kv_k = msa.HostResident(dev.kcache.cpu().pin_memory())
+        kv_v = msa.HostResident(dev.vcache.cpu().pin_memory())
     if decode:
         run = MSADecode(b, wl.Hkv, wl.G, wl.D, wl.k, P)
     elif query_major:
@@ -224,7 +233,7 @@ def main():
             elif name == "select":
                 run.select()
             elif name == "attend":
-                run.attend(dev.q, dev.kcache, dev.vcache, dev.scale)
+                run.attend(dev.q, kv_k, kv_v, dev.scale)
             else:
                 run.merge()
         if evs is not None:
@@ -269,8 +278,9 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": recorded_traffic(wl.name),
                 "algorithmic_bytes": score_bytes, "avg_ms": score_ms}
         attn_bytes = sel_tok * wl.D * 2 * 2                      # K and V rows of the selected tokens
-        roof_attn = {"kernel": "k_attn_decode+k_lse_merge", "bound": "hbm",
-                     "achieved": attn_bytes / (attend_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        roof_attn = {"kernel": "k_attn_decode+k_merge_splits", "bound": "host link" if kv_on_host else "hbm",
+                     "achieved": attn_bytes / (attend_ms * 1e-3) / 1e9,
+                     "peak": HOST_LINK_PEAK_GBS if kv_on_host else HBM_PEAK_GBS, "unit": "GB/s",
                      "algorithmic_bytes": attn_bytes, "avg_ms": attend_ms}
     else:
         sel_tok = selected_tokens(dev, run.sel, run.cnt)
@@ -307,7 +317,8 @@ def main():
                    "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "Di": wl.Di, "top_k": wl.k, "block": wl.block,
                    "l2_flush_between_steps": flush is not None,
                    "fused_index_topk": bool(args.fused_topk and not decode),
-                   "prefill_mode": None if decode else args.prefill_mode},
+                   "prefill_mode": None if decode else args.prefill_mode,
+                   "kv_on_host": bool(kv_on_host)},
         "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
         "roofline_detail": details,
         "stage_ms": {name: float(per_stage[:, i].mean()) for i, name in enumerate(stages)},

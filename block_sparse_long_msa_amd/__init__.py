@@ -13,17 +13,58 @@ import torch
 
 from ._lib import EXPORTS, MsaBatch, MsaCache, MSAError, check, load  # noqa: F401
 
-__all__ = ["Batch", "MSAError", "msa_index_score", "msa_index_topk", "msa_index_topk_workspace_size",
+__all__ = ["Batch", "HostResident", "MSAError", "msa_index_score", "msa_index_topk", "msa_index_topk_workspace_size",
            "msa_topk_blocks", "msa_build_sparse_page_table", "msa_topk_page_table",
            "msa_sparse_attn_decode", "msa_sparse_attn_decode_workspace_size", "msa_sparse_attn_prefill",
            "msa_sparse_attn_prefill_workspace_size", "msa_lse_merge", "msa_version", "load"]
 
 
-def _ptr(t: Optional[torch.Tensor], dtype, name: str, allow_none: bool = False) -> Optional[int]:
+_hip = None
+
+
+def _host_device_pointer(host_ptr: int) -> int:
+    """Device address of pinned host memory (hipHostGetDevicePointer)."""
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipHostGetDevicePointer.restype = ctypes.c_int
+        _hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+    dev = ctypes.c_void_p()
+    err = _hip.hipHostGetDevicePointer(ctypes.byref(dev), ctypes.c_void_p(host_ptr), 0)
+    if err != 0 or not dev.value:
+        raise RuntimeError(f"hipHostGetDevicePointer failed ({err}): the tensor is not device-accessible pinned memory")
+    return dev.value
+
+
+class HostResident:
+    """A pinned host tensor that the kernels read in place over the host link, e.g. K/V caches moved
+    out of HBM while the key-index cache stays resident: each decode step then fetches only the
+    selected blocks (the decoupled index/value offload that the Chinese page, section "遗留问题",
+    leaves as future work).  Wrap a tensor from ``t.pin_memory()`` or ``torch.empty(..., pin_memory=True)``;
+    it can be passed wherever a cache or K/V base tensor is expected."""
+
+    def __init__(self, t: torch.Tensor):
+        if t.is_cuda or not t.is_pinned():
+            raise ValueError("HostResident needs a pinned CPU tensor")
+        if not t.is_contiguous():
+            raise ValueError("HostResident needs a contiguous tensor")
+        self.tensor = t
+        self.shape, self.dtype = t.shape, t.dtype
+        self.device_ptr = _host_device_pointer(t.data_ptr())
+
+    def dim(self) -> int:
+        return self.tensor.dim()
+
+
+def _ptr(t, dtype, name: str, allow_none: bool = False) -> Optional[int]:
     if t is None:
         if allow_none:
             return None
         raise ValueError(f"{name} is required")
+    if isinstance(t, HostResident):
+        if t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        return t.device_ptr
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if t.dtype != dtype:
@@ -39,7 +80,7 @@ def _stream(stream) -> Optional[int]:
     return getattr(stream, "cuda_stream", stream)
 
 
-def _cache(t: torch.Tensor, name: str) -> MsaCache:
+def _cache(t, name: str) -> MsaCache:
     if t.dim() != 4:
         raise ValueError(f"{name} must be [pages, block, heads, dim]")
     P, BS, H, D = t.shape
