@@ -38,6 +38,8 @@ CASES = {
     # rows beyond the register layouts (> 16384 blocks): the radix-pass top-k, 16 waves per row,
     # and the two-launch form of msa_topk_page_table
     "topk_radix_long_rows": dict(ctx=[2100000], nq=[1], Hq=4, Hkv=1, D=64, Di=64, k=9),
+    # the largest k and G: a row split into up to 64 page runs, merged over 64 parts
+    "k64_g16_split": dict(ctx=[9000, 8300], nq=[1, 1], Hq=32, Hkv=2, D=128, Di=64, k=64),
 }
 GPU_DRAWN = {"topk_16_waves", "topk_radix_long_rows"}   # inputs drawn on the GPU, copied to the host
 

@@ -22,6 +22,11 @@ CASES = {
     "g16_d64": dict(ctx=[900, 520], nq=[400, 130], Hq=32, Hkv=2, D=64, Di=128, k=3),
     "g1_d128": dict(ctx=[640], nq=[640], Hq=4, Hkv=4, D=128, Di=128, k=2),
     "g2_k_over_candidates": dict(ctx=[400, 129], nq=[250, 129], Hq=4, Hkv=2, D=64, Di=64, k=8),
+    # the largest k and G the library takes: 64 slots per row, 64 parts x 16 heads in the merge
+    "k64_g16": dict(ctx=[9000], nq=[300], Hq=32, Hkv=2, D=64, Di=64, k=64),
+    # many short requests in one chunk: work items from many buckets, rows of many requests
+    "many_requests": dict(ctx=[300 + 37 * i for i in range(40)], nq=[1 + (i % 7) * 9 for i in range(40)], Hq=16,
+                          Hkv=4, D=128, Di=64, k=3),
 }
 
 
