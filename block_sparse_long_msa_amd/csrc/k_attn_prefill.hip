@@ -157,6 +157,78 @@ __global__ __launch_bounds__(256) void k_remap_fill(int64_t E, int B, int Hkv, i
   entries[slot] = t * 64 + j;
 }
 
+// The same count and scatter with the atomics aggregated in LDS, when every bucket fits in one
+// workgroup's histogram: a workgroup counts its run of entries into LDS and adds one total per
+// touched bucket to the global counts; the scatter recounts the run, reserves one range per
+// touched bucket with a single global atomic, and places its entries with LDS atomics.  The
+// popular buckets (hundreds of queries picking the same block) then see one global atomic per
+// workgroup instead of one per entry.
+constexpr int kLdsBuckets = 16384;  // buckets one LDS histogram holds (64 KiB)
+constexpr int kRemapRun = 16384;    // entries per workgroup
+
+__device__ __forceinline__ int remap_bucket(int64_t idx, int B, int Hkv, int k, int max_blocks,
+                                            const int32_t* __restrict__ cu_q, const int32_t* __restrict__ sel,
+                                            const int32_t* __restrict__ cnt, int& t, int& j) {
+  const int64_t tg = idx / k;
+  j = (int)(idx % k);
+  t = (int)(tg / Hkv);
+  if (j >= cnt[tg]) return -1;
+  const int g = (int)(tg % Hkv);
+  const int r = request_of(cu_q, B, t);
+  return (g * B + r) * max_blocks + sel[idx];
+}
+
+__global__ __launch_bounds__(256) void k_remap_count_lds(int64_t E, int B, int Hkv, int k, int G, int max_blocks,
+                                                         int NB, const int32_t* __restrict__ cu_q,
+                                                         const int32_t* __restrict__ sel,
+                                                         const int32_t* __restrict__ cnt, int32_t* __restrict__ counts,
+                                                         float* __restrict__ part_lse) {
+  __shared__ int hist[kLdsBuckets];
+  for (int i = threadIdx.x; i < NB; i += 256) hist[i] = 0;
+  __syncthreads();
+  const int64_t e0 = (int64_t)blockIdx.x * kRemapRun, e1 = min(e0 + kRemapRun, E);
+  for (int64_t idx = e0 + threadIdx.x; idx < e1; idx += 256) {
+    int t, j;
+    const int bucket = remap_bucket(idx, B, Hkv, k, max_blocks, cu_q, sel, cnt, t, j);
+    if (bucket >= 0) {
+      atomicAdd(&hist[bucket], 1);
+    } else {
+      for (int h = 0; h < G; ++h) part_lse[idx * G + h] = neg_inf();
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < NB; i += 256)
+    if (hist[i]) atomicAdd(&counts[i], hist[i]);
+}
+
+__global__ __launch_bounds__(256) void k_remap_fill_lds(int64_t E, int B, int Hkv, int k, int max_blocks, int NB,
+                                                        const int32_t* __restrict__ cu_q,
+                                                        const int32_t* __restrict__ sel,
+                                                        const int32_t* __restrict__ cnt,
+                                                        const int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ cursor, int32_t* __restrict__ entries) {
+  __shared__ int hist[kLdsBuckets];  // this run's count per bucket, then its next free slot
+  for (int i = threadIdx.x; i < NB; i += 256) hist[i] = 0;
+  __syncthreads();
+  const int64_t e0 = (int64_t)blockIdx.x * kRemapRun, e1 = min(e0 + kRemapRun, E);
+  for (int64_t idx = e0 + threadIdx.x; idx < e1; idx += 256) {
+    int t, j;
+    const int bucket = remap_bucket(idx, B, Hkv, k, max_blocks, cu_q, sel, cnt, t, j);
+    if (bucket >= 0) atomicAdd(&hist[bucket], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < NB; i += 256) {
+    const int c = hist[i];
+    if (c) hist[i] = offsets[i] + atomicAdd(&cursor[i], c);
+  }
+  __syncthreads();
+  for (int64_t idx = e0 + threadIdx.x; idx < e1; idx += 256) {
+    int t, j;
+    const int bucket = remap_bucket(idx, B, Hkv, k, max_blocks, cu_q, sel, cnt, t, j);
+    if (bucket >= 0) entries[atomicAdd(&hist[bucket], 1)] = t * 64 + j;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_remap_items(int64_t NB, const int32_t* __restrict__ counts,
                                                      const int32_t* __restrict__ item_off, int2* __restrict__ items) {
   const int64_t bucket = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -437,11 +509,21 @@ hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blo
   hipLaunchKernelGGL(k_fill_i32, dim3(fill_blocks), dim3(256), 0, stream, ws.counts, NB, 0);
   hipLaunchKernelGGL(k_fill_i32, dim3(fill_blocks), dim3(256), 0, stream, ws.cursor, NB, 0);
   const unsigned eb = (unsigned)((E + 255) / 256);
-  hipLaunchKernelGGL(k_remap_count, dim3(eb), dim3(256), 0, stream, E, B, Hkv, k, G, max_blocks, cu_q, sel, cnt,
-                     ws.counts, part_lse);
+  const bool lds_remap = NB <= kLdsBuckets;
+  const unsigned rb = (unsigned)((E + kRemapRun - 1) / kRemapRun);
+  if (lds_remap)
+    hipLaunchKernelGGL(k_remap_count_lds, dim3(rb), dim3(256), 0, stream, E, B, Hkv, k, G, max_blocks, (int)NB, cu_q,
+                       sel, cnt, ws.counts, part_lse);
+  else
+    hipLaunchKernelGGL(k_remap_count, dim3(eb), dim3(256), 0, stream, E, B, Hkv, k, G, max_blocks, cu_q, sel, cnt,
+                       ws.counts, part_lse);
   hipLaunchKernelGGL(k_remap_scan, dim3(1), dim3(1024), 0, stream, NB, ws.counts, ws.offsets, ws.item_off);
-  hipLaunchKernelGGL(k_remap_fill, dim3(eb), dim3(256), 0, stream, E, B, Hkv, k, max_blocks, cu_q, sel, cnt,
-                     ws.offsets, ws.cursor, ws.entries);
+  if (lds_remap)
+    hipLaunchKernelGGL(k_remap_fill_lds, dim3(rb), dim3(256), 0, stream, E, B, Hkv, k, max_blocks, (int)NB, cu_q, sel,
+                       cnt, ws.offsets, ws.cursor, ws.entries);
+  else
+    hipLaunchKernelGGL(k_remap_fill, dim3(eb), dim3(256), 0, stream, E, B, Hkv, k, max_blocks, cu_q, sel, cnt,
+                       ws.offsets, ws.cursor, ws.entries);
   hipLaunchKernelGGL(k_remap_items, dim3((unsigned)((NB + 255) / 256)), dim3(256), 0, stream, NB, ws.counts,
                      ws.item_off, ws.items);
   // upper bound on the work items, rounded up to whole XCD rounds

@@ -27,6 +27,8 @@ CASES = {
     # many short requests in one chunk: work items from many buckets, rows of many requests
     "many_requests": dict(ctx=[300 + 37 * i for i in range(40)], nq=[1 + (i % 7) * 9 for i in range(40)], Hq=16,
                           Hkv=4, D=128, Di=64, k=3),
+    # more (KV head, request, block) buckets than one LDS histogram holds: the remap's global-atomic path
+    "remap_many_buckets": dict(ctx=[100000, 90000, 50000], nq=[10, 5, 20], Hq=16, Hkv=8, D=64, Di=64, k=8),
 }
 
 
