@@ -21,8 +21,13 @@
 #ifndef MSA_SCORE_PREFETCH
 #define MSA_SCORE_PREFETCH 2
 #endif
+#ifndef MSA_SCORE_BPW
+#define MSA_SCORE_BPW 2
+#endif
 
 namespace msa {
+
+constexpr int kScoreBPW = MSA_SCORE_BPW;  // key-index blocks per workgroup of the staged decode scorer
 
 // Operands of one KV head for the decode scorer: the wave's two 16-token key-index tiles and
 // the (zero-padded) query index fragments.
@@ -141,13 +146,16 @@ __global__ __launch_bounds__(256, 2) void k_score_decode_lds(
   constexpr int GPW = 256 / DI;           // KV heads per wave at most (Hkv * DI <= 1024)
   constexpr int LPT = kStageBytes / 16 / 256;  // 16-byte loads per thread per slice (8)
   __shared__ __attribute__((aligned(16))) unsigned char stage[2][kStageLdsBytes];
-  const int b = blockIdx.x, r = blockIdx.y;
+  const int r = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, qd = lane >> 4;
   const int q0 = cu_q[r], nq = cu_q[r + 1] - q0, L = ctx_len[r];
   const int RB = Hkv * DI * 2;            // bytes per token row (all KV heads)
   const int RBP = RB + 16;                // padded LDS row
   const int slice_bytes = 16 * RB;
 
+  for (int bi = 0; bi < kScoreBPW; ++bi) {  // kScoreBPW consecutive blocks of the request per workgroup
+  const int b = blockIdx.x * kScoreBPW + bi;
+  if (b >= max_blocks) break;
   for (int qc = 0; qc < nq; qc += 16) {
     const int nqc = min(16, nq - qc);
     const bool qvalid = n < nqc;
@@ -175,8 +183,9 @@ __global__ __launch_bounds__(256, 2) void k_score_decode_lds(
     for (int gi = 0; gi < GPW; ++gi) {
       const int g = w + 4 * gi;
 #pragma unroll
-      for (int kw = 0; kw < KW; ++kw)
-        qf[gi][kw] = g < Hkv ? ld16(q_idx + ((int64_t)my_t * Hkv + g) * DI + 32 * kw + 8 * qd) & qmask : zero4();
+      for (int kw = 0; kw < KW; ++kw)  // unconditional loads (clamped head), zeroed by mask: no branch per load
+        qf[gi][kw] = ld16(q_idx + ((int64_t)my_t * Hkv + min(g, Hkv - 1)) * DI + 32 * kw + 8 * qd) &
+                     (g < Hkv ? qmask : 0u);
     }
     float mx[GPW];
 #pragma unroll
@@ -238,6 +247,7 @@ __global__ __launch_bounds__(256, 2) void k_score_decode_lds(
       if (g < Hkv && qd == 0 && qvalid) scores[((int64_t)(q0 + qc + n) * Hkv + g) * max_blocks + b] = m;
     }
   }
+  }
 }
 
 constexpr int kPrefTQ = 256;  // query rows per workgroup (64 per wave)
@@ -284,7 +294,8 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
       if (in) { pmax = max(pmax, pos[nt]); pmin = min(pmin, pos[nt]); }
 #pragma unroll
       for (int kw = 0; kw < KW; ++kw)
-        qf[nt][kw] = in ? ld16(q_idx + ((int64_t)row * Hkv + g) * DI + 32 * kw + 8 * qd) : zero4();
+        qf[nt][kw] = ld16(q_idx + ((int64_t)(in ? row : qa) * Hkv + g) * DI + 32 * kw + 8 * qd) &
+                     (in ? 0xffffffffu : 0u);  // rows outside the request read a valid row, zeroed
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
@@ -473,6 +484,7 @@ hipError_t launch_score_decode(int B, int Di, const int32_t* block_table, int ma
   const bf16* qi = static_cast<const bf16*>(q_idx);
   const bf16* ki = static_cast<const bf16*>(kidx);
   if (Hkv * Di <= 1024) {
+    grid.x = (max_blocks + kScoreBPW - 1) / kScoreBPW;
     if (Di == 128)
       hipLaunchKernelGGL(k_score_decode_lds<128>, grid, block, 0, stream, block_table, max_blocks, ctx_len, cu_q,
                          q_pos, qi, ki, Hkv, scores);
