@@ -387,3 +387,61 @@ def test_pins_catch_missing_softmax_scale(monkeypatch):
     mask = np.arange(70)[None, :] <= x.q_pos[:, None]
     ref = _sdpa(x.q[:, 0].astype(np.float64), K[:, 0], V[:, 0], mask, 1.0 / math.sqrt(8))
     assert not np.allclose(out[:, 0], ref, atol=1e-6)
+
+
+def test_pins_catch_reversed_tie_rule(monkeypatch):
+    """A top-k that prefers the higher block id among equal scores fails the defining property."""
+    orig = np.lexsort
+
+    def lexsort_higher_id_first(keys):
+        ids, neg_s = keys
+        return orig((-np.asarray(ids), neg_s))
+    monkeypatch.setattr(oracle.msa_oracle.np, "lexsort", lexsort_higher_id_first)
+    vals = np.asarray([1.0, 2.0, 1.0, 1.0, 0.0])          # three-way tie at the boundary for k = 2
+    scores = np.full((1, 1, 8), -np.inf)
+    scores[0, 0, :5] = vals
+    sel, cnt = oracle.topk_blocks(scores, np.asarray([4 * 4]), 4, 2)
+    assert sel[0, 0, :cnt[0, 0]].tolist() != _topk_by_definition(vals, 2)
+
+
+def test_pins_catch_base2_lse(monkeypatch):
+    """A merge that takes log2 of the weight sum no longer equals one softmax over the union."""
+    monkeypatch.setattr(oracle.msa_oracle.np, "log", np.log2)
+    x = _tiny([300, 90], [20, 7], k=3, D=8, Di=4, seed=15)
+    _, sel, cnt = _select(x)
+    po, pl = oracle.block_partials(x.q, x.kcache, x.vcache, x.block_table, x.ctx_len, x.q_req, x.q_pos,
+                                   sel, cnt, x.wl.block, x.scale)
+    _, l2 = oracle.lse_merge(po, pl)
+    monkeypatch.undo()
+    _, lse = _attend(x, sel, cnt)
+    assert not np.allclose(l2.reshape(lse.shape), lse, atol=1e-6)
+
+
+def test_pins_catch_mean_block_score(monkeypatch):
+    """Reducing a block by the mean of its tokens' dots instead of the max fails the brute force."""
+    monkeypatch.setattr(oracle.msa_oracle, "block_score",
+                        lambda q_vec, k_rows, n_valid: float(np.mean(k_rows[:n_valid] @ q_vec)))
+    x = _tiny([37, 70], [5, 3], seed=1)
+    got = _scores(x)
+    monkeypatch.undo()
+    ref = _bruteforce_scores(x)
+    fin = np.isfinite(ref)
+    assert not np.allclose(got[fin], ref[fin], atol=1e-9)
+
+
+def test_pins_catch_page_id_without_head_stride():
+    """A virtual page id of block_table*block + g (forgetting the factor Hkv) addresses other rows:
+    the as_strided round trip pin fails on it."""
+    x = _tiny([300, 47], [1, 1], k=3, D=8, seed=16)
+    _, sel, cnt = _select(x)
+    Hkv, BS, D = x.wl.Hkv, x.wl.block, x.wl.D
+    flat = torch.from_numpy(x.kcache).reshape(-1)
+    mismatches = 0
+    for t in range(2):
+        for g in range(Hkv):
+            for j in range(cnt[t, g]):
+                page = int(x.block_table[int(x.q_req[t]), sel[t, g, j]])
+                v = page * BS + g                                  # the planted mistake
+                view = torch.as_strided(flat, (BS, D), (Hkv * D, 1), storage_offset=v * D)
+                mismatches += not torch.equal(view, torch.from_numpy(x.kcache[page, :, g, :]))
+    assert mismatches > 0
