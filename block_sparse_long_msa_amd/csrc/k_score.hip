@@ -127,15 +127,22 @@ __global__ __launch_bounds__(256) void k_score_decode(
 }
 
 // LDS-staged decode scorer, used when one 16-token slice of a page (16 * Hkv * Di * 2 bytes) fits a
-// 32 KiB stage, i.e. Hkv * Di <= 1024.  The page is streamed with fully coalesced 16-byte
+// 32 KiB stage, i.e. Hkv * Di <= 1024.  A workgroup takes kScoreBPW consecutive blocks of one
+// request and streams their context slices as one sequence with fully coalesced 16-byte
 // non-temporal loads (each wave instruction reads 1 KiB of consecutive bytes), two slices ahead in
-// registers, and stored into a double-buffered LDS stage whose token rows are padded by 16 bytes so
-// that the MFMA operand reads (16 token rows, same column) are bank-conflict free.  Wave w owns KV
-// heads w, w+4, ...: it reads their operands from LDS and keeps their running block max in
-// registers, so no cross-wave reduction is needed.
+// registers, into a double-buffered LDS stage whose token rows are padded by 16 bytes so that the
+// MFMA operand reads (16 token rows, same column) are bank-conflict free.  Every load and LDS store
+// of the stream is unconditional (indices past the end are clamped to the last slice, which is then
+// read again and never used), so the wait before a store covers exactly the slice being stored and
+// the next slice stays in flight.  Wave w owns KV heads w, w+4, ...: it reads their operands from LDS
+// and keeps their running block max in registers, so no cross-wave reduction is needed.
+//
+// Slices are chosen by the request's context length; token positions past a query's own position
+// are masked in the max (with queries at the end of the context, as in decode, nothing is read
+// that no query uses).
 constexpr int kStageBytes = 32768;
 constexpr int kStageLdsBytes = 16 * 16 + kStageBytes;  // + 16 B pad per token row
-constexpr int kStagePF = 2;                            // slices in flight in registers
+constexpr int kSlicesPerBlock = kBlock / 16;
 
 template <int DI>
 __global__ __launch_bounds__(256, 2) void k_score_decode_lds(
@@ -146,38 +153,58 @@ __global__ __launch_bounds__(256, 2) void k_score_decode_lds(
   constexpr int GPW = 256 / DI;           // KV heads per wave at most (Hkv * DI <= 1024)
   constexpr int LPT = kStageBytes / 16 / 256;  // 16-byte loads per thread per slice (8)
   __shared__ __attribute__((aligned(16))) unsigned char stage[2][kStageLdsBytes];
-  const int r = blockIdx.y;
+  const int r = blockIdx.y, b0 = blockIdx.x * kScoreBPW;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, qd = lane >> 4;
+  // independent loads first: the query range, the context length and the blocks' page ids
   const int q0 = cu_q[r], nq = cu_q[r + 1] - q0, L = ctx_len[r];
+  int page[kScoreBPW];
+#pragma unroll
+  for (int bi = 0; bi < kScoreBPW; ++bi) page[bi] = block_table[(int64_t)r * max_blocks + min(b0 + bi, max_blocks - 1)];
   const int RB = Hkv * DI * 2;            // bytes per token row (all KV heads)
   const int RBP = RB + 16;                // padded LDS row
   const int slice_bytes = 16 * RB;
+  // blocks of this workgroup (nblk) and those holding context tokens (nb); slices to stream (S)
+  const int nblk = min(kScoreBPW, max_blocks - b0);
+  const int nb = L > 0 ? max(0, min(nblk, (L - 1) / kBlock - b0 + 1)) : 0;
+  const int S = nb > 0 ? kSlicesPerBlock * (nb - 1) + min(L - 1 - (b0 + nb - 1) * kBlock, kBlock - 1) / 16 + 1 : 0;
 
-  for (int bi = 0; bi < kScoreBPW; ++bi) {  // kScoreBPW consecutive blocks of the request per workgroup
-  const int b = blockIdx.x * kScoreBPW + bi;
-  if (b >= max_blocks) break;
+  // this thread's 16-byte pieces of a slice: clamped offsets, so tails read (and store) the last piece again
+  int soff[LPT], loff[LPT];
+#pragma unroll
+  for (int u = 0; u < LPT; ++u) {
+    const int off = min(16 * (tid + 256 * u), slice_bytes - 16);
+    soff[u] = off;
+    loff[u] = (off / RB) * RBP + off % RB;
+  }
+  auto slice_src = [&](int gs) {  // global slice gs (clamped by the caller) of the stream
+    const int bi = gs / kSlicesPerBlock, sl = gs % kSlicesPerBlock;
+    int pg = page[0];
+#pragma unroll
+    for (int j = 1; j < kScoreBPW; ++j) pg = bi == j ? page[j] : pg;
+    return reinterpret_cast<const unsigned char*>(kidx) + ((int64_t)pg * kBlock * RB + (int64_t)sl * slice_bytes);
+  };
+  auto load_slice = [&](u32x4 (&reg)[LPT], int gs) {
+    const unsigned char* src = slice_src(min(gs, S - 1));
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) reg[u] = ld16_nt(src + soff[u]);
+  };
+  auto store_slice = [&](const u32x4 (&reg)[LPT], int buf) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) st16(&stage[buf][loff[u]], reg[u]);
+  };
+
   for (int qc = 0; qc < nq; qc += 16) {
     const int nqc = min(16, nq - qc);
+    for (int e = tid; e < (nblk - nb) * nqc * Hkv; e += 256) {  // blocks with no context token
+      const int bi = nb + e / (nqc * Hkv), t = q0 + qc + (e / Hkv) % nqc, g = e % Hkv;
+      scores[((int64_t)t * Hkv + g) * max_blocks + b0 + bi] = neg_inf();
+    }
+    if (S == 0) continue;
     const bool qvalid = n < nqc;
     const int my_t = q0 + qc + (qvalid ? n : 0);
-    const int pos = qvalid ? q_pos[my_t] : -1;
     const uint32_t qmask = qvalid ? 0xffffffffu : 0u;
-    int maxpos = pos;
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) maxpos = max(maxpos, __shfl_xor(maxpos, m, kWave));
-    if (b * kBlock > maxpos) {
-      for (int e = tid; e < nqc * Hkv; e += 256) {
-        const int t = q0 + qc + e / Hkv, g = e % Hkv;
-        scores[((int64_t)t * Hkv + g) * max_blocks + b] = neg_inf();
-      }
-      continue;
-    }
-    // slices holding at least one token that some query of the chunk may use
-    const int last_tok = min(min(maxpos, L - 1) - b * kBlock, kBlock - 1);
-    const int nsl = last_tok / 16 + 1;
-    const int page = block_table[(int64_t)r * max_blocks + b];
-    const unsigned char* src = reinterpret_cast<const unsigned char*>(kidx) + (int64_t)page * kBlock * RB;
 
+    // query operands first, so that the wait for slice 0 below also covers them
     u32x4 qf[GPW][KW];
 #pragma unroll
     for (int gi = 0; gi < GPW; ++gi) {
@@ -187,33 +214,23 @@ __global__ __launch_bounds__(256, 2) void k_score_decode_lds(
         qf[gi][kw] = ld16(q_idx + ((int64_t)my_t * Hkv + min(g, Hkv - 1)) * DI + 32 * kw + 8 * qd) &
                      (g < Hkv ? qmask : 0u);
     }
+    const int pos_t = q_pos[my_t];  // unconditional (padded lanes read a real row)
+    asm volatile("" ::"v"(pos_t));
+    const int pos = qvalid ? pos_t : -1;
     float mx[GPW];
 #pragma unroll
     for (int gi = 0; gi < GPW; ++gi) mx[gi] = neg_inf();
 
-    auto load_slice = [&](u32x4 (&reg)[LPT], int sl) {
-#pragma unroll
-      for (int u = 0; u < LPT; ++u) {
-        const int off = 16 * (tid + 256 * u);
-        reg[u] = off < slice_bytes ? ld16_nt(src + (int64_t)sl * slice_bytes + off) : zero4();
-      }
-    };
-    auto store_slice = [&](const u32x4 (&reg)[LPT], int buf) {
-#pragma unroll
-      for (int u = 0; u < LPT; ++u) {
-        const int off = 16 * (tid + 256 * u);
-        if (off < slice_bytes) st16(&stage[buf][(off / RB) * RBP + off % RB], reg[u]);
-      }
-    };
-    u32x4 regs[kStagePF][LPT];
+    u32x4 regs[2][LPT];
     load_slice(regs[0], 0);
-    if (nsl > 1) load_slice(regs[1], 1);
+    load_slice(regs[1], 1);
     store_slice(regs[0], 0);
-    if (nsl > 2) load_slice(regs[0], 2);
+    load_slice(regs[0], 2);
     __syncthreads();
 
-    // slice sl is in stage[sl & 1]; the registers regs[(sl + 1) & 1] hold slice sl + 1
-    auto step = [&](int sl, int buf, u32x4 (&reg)[LPT]) {
+    auto compute = [&](int gs, int buf) {  // slice gs, staged in stage[buf]
+      const int bi = gs / kSlicesPerBlock, sl = gs % kSlicesPerBlock;
+      const int b = b0 + bi;
 #pragma unroll
       for (int gi = 0; gi < GPW; ++gi) {
         const int g = w + 4 * gi;
@@ -229,24 +246,42 @@ __global__ __launch_bounds__(256, 2) void k_score_decode_lds(
           for (int i = 0; i < 4; ++i) mx[gi] = (s0 + i <= pos && s0 + i < L) ? fmaxf(mx[gi], acc[i]) : mx[gi];
         }
       }
-      __syncthreads();  // stage[buf ^ 1] (slice sl - 1) is no longer read
-      if (sl + 1 < nsl) {
-        store_slice(reg, buf ^ 1);
-        if (sl + 3 < nsl) load_slice(reg, sl + 3);
+      if (sl == kSlicesPerBlock - 1 || gs == S - 1) {  // the block's last slice: write its scores
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi) {
+          const int g = w + 4 * gi;
+          const float m = max_over_quads(mx[gi]);
+          if (g < Hkv && qd == 0 && qvalid) scores[((int64_t)(q0 + qc + n) * Hkv + g) * max_blocks + b] = m;
+          mx[gi] = neg_inf();
+        }
       }
+    };
+    // after compute(gs, buf): stage the next slice (held in reg) and, if asked, load slice `next` into reg
+    auto advance = [&](int buf, u32x4 (&reg)[LPT], int next) {
+      __syncthreads();  // stage[buf ^ 1] (slice gs - 1) is no longer read
+      store_slice(reg, buf ^ 1);
+      if (next >= 0) load_slice(reg, next);
       __syncthreads();
     };
-    for (int sl = 0; sl < nsl; sl += 2) {
-      step(sl, 0, regs[1]);
-      if (sl + 1 < nsl) step(sl + 1, 1, regs[0]);
+    // Main loop: at the top, stage[0] holds slice gs and regs[1], regs[0] hold (or are loading)
+    // slices gs + 1 and gs + 2.  Every step loads a slice that exists, so the outstanding loads are
+    // in the same order on every path into the loop head.
+    int gs = 0;
+    for (; gs + 4 < S; gs += 2) {
+      compute(gs, 0);
+      advance(0, regs[1], gs + 3);
+      compute(gs + 1, 1);
+      advance(1, regs[0], gs + 4);
     }
-#pragma unroll
-    for (int gi = 0; gi < GPW; ++gi) {
-      const int g = w + 4 * gi;
-      const float m = max_over_quads(mx[gi]);
-      if (g < Hkv && qd == 0 && qvalid) scores[((int64_t)(q0 + qc + n) * Hkv + g) * max_blocks + b] = m;
-    }
-  }
+    // the last R = S - gs (1..4) slices; only slice gs + 3 (if R = 4) remains to be loaded
+    const int R = S - gs;
+    compute(gs, 0);
+    if (R > 1) advance(0, regs[1], R == 4 ? gs + 3 : -1);
+    if (R > 1) compute(gs + 1, 1);
+    if (R > 2) advance(1, regs[0], -1);
+    if (R > 2) compute(gs + 2, 0);
+    if (R > 3) advance(0, regs[1], -1);
+    if (R > 3) compute(gs + 3, 1);
   }
 }
 
@@ -273,7 +308,9 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
   __shared__ int wred[2][4];
 
   const int g = blockIdx.x % Hkv;  // consecutive workgroups take consecutive KV heads
-  const int row0 = (blockIdx.x / Hkv) * kPrefTQ;
+  // Row tiles go from the last to the first: a request's later rows have longer causal ranges, so
+  // the longest tiles start first and the short ones fill the end of the launch.
+  const int row0 = ((int)gridDim.x / Hkv - 1 - (int)blockIdx.x / Hkv) * kPrefTQ;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, qd = lane >> 4;
   const int last_row = min(row0 + kPrefTQ, Nq) - 1;
   const int r_first = request_of(cu_q, B, row0), r_last = request_of(cu_q, B, last_row);

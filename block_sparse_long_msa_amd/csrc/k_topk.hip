@@ -261,17 +261,25 @@ __global__ __launch_bounds__(64 * NW) void k_topk_reg(int Hkv, int max_blocks, c
     }
     return c;
   };
+  // T: the largest threshold with at least k keys >= T found so far.  The search stops early once
+  // exactly k keys are >= T: those are the top k, whatever T's low bits (with a tie across the
+  // boundary it runs down to bit 0 and T is the k-th largest key).
   uint32_t T = kmin;
+  int parity = 0;  // buffer of the next count (alternates, so a slow wave's read is never overwritten)
   if (kmin != kmax) {
     const int hb = 31 - __builtin_clz(kmin ^ kmax);
     T = hb == 31 ? 0u : (kmin & ~((2u << hb) - 1u));
     for (int b = hb; b >= 0; --b) {  // every trial threshold is >= 1, so id slots past n never count
       const uint32_t cand = T | (1u << b);
-      if (count_ge(cand, b & 1) >= k) T = cand;
+      const int c = count_ge(cand, parity);
+      parity ^= 1;
+      if (c >= k) {
+        T = cand;
+        if (c == k) break;
+      }
     }
   }
-  // parity 1: the last bisection step (b = 0) used buffer 0, which a slow wave may still be reading
-  const int remaining = k - (T == 0xffffffffu ? 0 : count_ge(T + 1u, 1));
+  const int remaining = k - (T == 0xffffffffu ? 0 : count_ge(T + 1u, parity));
 
   // emit in id order: keys above T, then the first `remaining` keys equal to T
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
