@@ -66,6 +66,23 @@ def _run(dev, max_q=None):
 def test_decode_path_matches_oracle(name):
     announce("decode", name)
     dev, cpu = setup(_wl(name), on_gpu_generation=name in GPU_DRAWN, host_copy=True)
+    _check_against_oracle(dev, cpu)
+
+
+def test_queries_before_the_context_end():
+    """Queries placed well before their request's last cached token: the blocks after every query's
+    position but inside the context are streamed by the decode scorer with all of their tokens
+    masked, so they must come out -inf, and attention stops at each query's own position."""
+    announce("decode", "queries before the context end")
+    dev, cpu = setup(_wl("multi_query", seed=9))
+    pos, cu = cpu.q_pos.clone(), cpu.cu_q.numpy()
+    for r, back in enumerate((2200, 0, 901)):     # contexts 4000, 300, 2000
+        pos[cu[r]:cu[r + 1]] -= back
+    cpu.q_pos, dev.q_pos = pos, pos.cuda()
+    _check_against_oracle(dev, cpu)
+
+
+def _check_against_oracle(dev, cpu):
     x = np_inputs(cpu)
     wl = dev.wl
     s, sel, cnt, pt, rl, out, lse = [host(t) for t in _run(dev)]
