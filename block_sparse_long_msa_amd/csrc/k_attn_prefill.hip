@@ -163,37 +163,89 @@ __global__ __launch_bounds__(256) void k_remap_fill(int64_t E, int B, int Hkv, i
 // touched bucket with a single global atomic, and places its entries with LDS atomics.  The
 // popular buckets (hundreds of queries picking the same block) then see one global atomic per
 // workgroup instead of one per entry.
+//
+// Each thread takes its entries kRemapU at a time with every cnt/sel load of the batch issued
+// before any is used (indices past the run are clamped and their results dropped), and finds the
+// request of a row in a copy of cu_q held in LDS, so a run costs a few round trips, not one chain
+// of dependent loads per entry.  Small problems use shorter runs, so that more workgroups share
+// the latency.
 constexpr int kLdsBuckets = 16384;  // buckets one LDS histogram holds (64 KiB)
-constexpr int kRemapRun = 16384;    // entries per workgroup
+constexpr int kRemapU = 8;          // entries per thread per batch
+constexpr int kRemapMaxRun = 16384; // entries per workgroup, at most (a multiple of 256 * kRemapU)
+constexpr int kLdsCu = 2048;        // requests whose cu_q fits the LDS copy
 
-__device__ __forceinline__ int remap_bucket(int64_t idx, int B, int Hkv, int k, int max_blocks,
-                                            const int32_t* __restrict__ cu_q, const int32_t* __restrict__ sel,
-                                            const int32_t* __restrict__ cnt, int& t, int& j) {
-  const int64_t tg = idx / k;
-  j = (int)(idx % k);
-  t = (int)(tg / Hkv);
-  if (j >= cnt[tg]) return -1;
-  const int g = (int)(tg % Hkv);
-  const int r = request_of(cu_q, B, t);
-  return (g * B + r) * max_blocks + sel[idx];
+int remap_run(int64_t E) {
+  int run = kRemapMaxRun;
+  while (run > 256 * kRemapU && (E + run - 1) / run < 256) run >>= 1;
+  return run;
 }
 
-__global__ __launch_bounds__(256) void k_remap_count_lds(int64_t E, int B, int Hkv, int k, int G, int max_blocks,
-                                                         int NB, const int32_t* __restrict__ cu_q,
-                                                         const int32_t* __restrict__ sel,
-                                                         const int32_t* __restrict__ cnt, int32_t* __restrict__ counts,
-                                                         float* __restrict__ part_lse) {
+struct RemapArgs {
+  int64_t E;
+  int B, Hkv, k, max_blocks;
+  const int32_t* cu_q;
+  const int32_t* sel;
+  const int32_t* cnt;
+};
+
+// Request of row t: binary search over cu_q[0..B], from the LDS copy when there is one.
+__device__ __forceinline__ int remap_request(const RemapArgs& a, const int32_t* s_cu, int t) {
+  int lo = 0, hi = a.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const int c = a.B <= kLdsCu ? s_cu[mid] : a.cu_q[mid];
+    if (c <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ void remap_load_cu(const RemapArgs& a, int32_t* s_cu) {
+  if (a.B <= kLdsCu)
+    for (int i = threadIdx.x; i <= a.B; i += 256) s_cu[i] = a.cu_q[i];
+}
+
+// One batch of this thread's entries base + 256*u: bucket (or -1 for an empty slot j >= cnt, or
+// -2 past the run's end) and the entry's code t*64 + j.
+__device__ __forceinline__ void remap_batch(const RemapArgs& a, const int32_t* s_cu, int64_t base, int64_t e1,
+                                            int (&bucket)[kRemapU], int (&code)[kRemapU]) {
+  // entry indices fit in int32 (the entry count is checked on the host)
+  int c[kRemapU], sv[kRemapU], tg[kRemapU], ic[kRemapU];
+#pragma unroll
+  for (int u = 0; u < kRemapU; ++u) {
+    ic[u] = (int)min(base + 256 * u, e1 - 1);
+    tg[u] = ic[u] / a.k;
+    c[u] = a.cnt[tg[u]];
+    sv[u] = a.sel[ic[u]];
+  }
+#pragma unroll
+  for (int u = 0; u < kRemapU; ++u) {
+    const int j = ic[u] - tg[u] * a.k, t = tg[u] / a.Hkv, g = tg[u] - t * a.Hkv;
+    code[u] = t * 64 + j;
+    if (base + 256 * u >= e1) bucket[u] = -2;
+    else if (j >= c[u]) bucket[u] = -1;
+    else bucket[u] = (g * a.B + remap_request(a, s_cu, t)) * a.max_blocks + sv[u];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_remap_count_lds(RemapArgs a, int run, int G, int NB,
+                                                         int32_t* __restrict__ counts, float* __restrict__ part_lse) {
   __shared__ int hist[kLdsBuckets];
+  __shared__ int32_t s_cu[kLdsCu + 1];
   for (int i = threadIdx.x; i < NB; i += 256) hist[i] = 0;
+  remap_load_cu(a, s_cu);
   __syncthreads();
-  const int64_t e0 = (int64_t)blockIdx.x * kRemapRun, e1 = min(e0 + kRemapRun, E);
-  for (int64_t idx = e0 + threadIdx.x; idx < e1; idx += 256) {
-    int t, j;
-    const int bucket = remap_bucket(idx, B, Hkv, k, max_blocks, cu_q, sel, cnt, t, j);
-    if (bucket >= 0) {
-      atomicAdd(&hist[bucket], 1);
-    } else {
-      for (int h = 0; h < G; ++h) part_lse[idx * G + h] = neg_inf();
+  const int64_t e0 = (int64_t)blockIdx.x * run, e1 = min(e0 + run, a.E);
+  for (int64_t base = e0 + threadIdx.x; base < e1; base += 256 * kRemapU) {
+    int bucket[kRemapU], code[kRemapU];
+    remap_batch(a, s_cu, base, e1, bucket, code);
+#pragma unroll
+    for (int u = 0; u < kRemapU; ++u) {
+      if (bucket[u] >= 0) {
+        atomicAdd(&hist[bucket[u]], 1);
+      } else if (bucket[u] == -1) {
+        const int64_t idx = base + 256 * u;
+        for (int h = 0; h < G; ++h) part_lse[idx * G + h] = neg_inf();
+      }
     }
   }
   __syncthreads();
@@ -201,20 +253,21 @@ __global__ __launch_bounds__(256) void k_remap_count_lds(int64_t E, int B, int H
     if (hist[i]) atomicAdd(&counts[i], hist[i]);
 }
 
-__global__ __launch_bounds__(256) void k_remap_fill_lds(int64_t E, int B, int Hkv, int k, int max_blocks, int NB,
-                                                        const int32_t* __restrict__ cu_q,
-                                                        const int32_t* __restrict__ sel,
-                                                        const int32_t* __restrict__ cnt,
+__global__ __launch_bounds__(256) void k_remap_fill_lds(RemapArgs a, int run, int NB,
                                                         const int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ cursor, int32_t* __restrict__ entries) {
   __shared__ int hist[kLdsBuckets];  // this run's count per bucket, then its next free slot
+  __shared__ int32_t s_cu[kLdsCu + 1];
   for (int i = threadIdx.x; i < NB; i += 256) hist[i] = 0;
+  remap_load_cu(a, s_cu);
   __syncthreads();
-  const int64_t e0 = (int64_t)blockIdx.x * kRemapRun, e1 = min(e0 + kRemapRun, E);
-  for (int64_t idx = e0 + threadIdx.x; idx < e1; idx += 256) {
-    int t, j;
-    const int bucket = remap_bucket(idx, B, Hkv, k, max_blocks, cu_q, sel, cnt, t, j);
-    if (bucket >= 0) atomicAdd(&hist[bucket], 1);
+  const int64_t e0 = (int64_t)blockIdx.x * run, e1 = min(e0 + run, a.E);
+  for (int64_t base = e0 + threadIdx.x; base < e1; base += 256 * kRemapU) {
+    int bucket[kRemapU], code[kRemapU];
+    remap_batch(a, s_cu, base, e1, bucket, code);
+#pragma unroll
+    for (int u = 0; u < kRemapU; ++u)
+      if (bucket[u] >= 0) atomicAdd(&hist[bucket[u]], 1);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < NB; i += 256) {
@@ -222,10 +275,12 @@ __global__ __launch_bounds__(256) void k_remap_fill_lds(int64_t E, int B, int Hk
     if (c) hist[i] = offsets[i] + atomicAdd(&cursor[i], c);
   }
   __syncthreads();
-  for (int64_t idx = e0 + threadIdx.x; idx < e1; idx += 256) {
-    int t, j;
-    const int bucket = remap_bucket(idx, B, Hkv, k, max_blocks, cu_q, sel, cnt, t, j);
-    if (bucket >= 0) entries[atomicAdd(&hist[bucket], 1)] = t * 64 + j;
+  for (int64_t base = e0 + threadIdx.x; base < e1; base += 256 * kRemapU) {
+    int bucket[kRemapU], code[kRemapU];
+    remap_batch(a, s_cu, base, e1, bucket, code);
+#pragma unroll
+    for (int u = 0; u < kRemapU; ++u)
+      if (bucket[u] >= 0) entries[atomicAdd(&hist[bucket[u]], 1)] = code[u];
   }
 }
 
@@ -510,17 +565,18 @@ hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blo
   hipLaunchKernelGGL(k_fill_i32, dim3(fill_blocks), dim3(256), 0, stream, ws.cursor, NB, 0);
   const unsigned eb = (unsigned)((E + 255) / 256);
   const bool lds_remap = NB <= kLdsBuckets;
-  const unsigned rb = (unsigned)((E + kRemapRun - 1) / kRemapRun);
+  const int run = remap_run(E);
+  const unsigned rb = (unsigned)((E + run - 1) / run);
+  const RemapArgs ra{E, B, Hkv, k, max_blocks, cu_q, sel, cnt};
   if (lds_remap)
-    hipLaunchKernelGGL(k_remap_count_lds, dim3(rb), dim3(256), 0, stream, E, B, Hkv, k, G, max_blocks, (int)NB, cu_q,
-                       sel, cnt, ws.counts, part_lse);
+    hipLaunchKernelGGL(k_remap_count_lds, dim3(rb), dim3(256), 0, stream, ra, run, G, (int)NB, ws.counts, part_lse);
   else
     hipLaunchKernelGGL(k_remap_count, dim3(eb), dim3(256), 0, stream, E, B, Hkv, k, G, max_blocks, cu_q, sel, cnt,
                        ws.counts, part_lse);
   hipLaunchKernelGGL(k_remap_scan, dim3(1), dim3(1024), 0, stream, NB, ws.counts, ws.offsets, ws.item_off);
   if (lds_remap)
-    hipLaunchKernelGGL(k_remap_fill_lds, dim3(rb), dim3(256), 0, stream, E, B, Hkv, k, max_blocks, (int)NB, cu_q, sel,
-                       cnt, ws.offsets, ws.cursor, ws.entries);
+    hipLaunchKernelGGL(k_remap_fill_lds, dim3(rb), dim3(256), 0, stream, ra, run, (int)NB, ws.offsets, ws.cursor,
+                       ws.entries);
   else
     hipLaunchKernelGGL(k_remap_fill, dim3(eb), dim3(256), 0, stream, E, B, Hkv, k, max_blocks, cu_q, sel, cnt,
                        ws.offsets, ws.cursor, ws.entries);
