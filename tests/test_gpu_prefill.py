@@ -52,6 +52,10 @@ def _run(dev):
 def test_prefill_path_matches_oracle(name):
     announce("prefill", name)
     dev, cpu = setup(_wl(name))
+    _check_against_oracle(dev, cpu)
+
+
+def _check_against_oracle(dev, cpu):
     x = np_inputs(cpu)
     wl = dev.wl
     s, sel, cnt, po, pl, out, lse = [host(t) for t in _run(dev)]
