@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--prefill-mode", default="kvbm", choices=["kvbm", "query-major"],
                    help="prefill attention: KV-block-major with LSE merge (the method), or the query-major "
                         "baseline it is measured against (each row reads its own blocks)")
+    p.add_argument("--decode-select", default="attend", choices=["attend", "page_table", "separate"],
+                   help="decode: top-k + page table + attention in one call after the scores (attend), or the "
+                        "top-k + page table call then the attention call (page_table), or all three calls")
     p.add_argument("--kv-on-host", action="store_true",
                    help="decode: keep the key-index cache in HBM but move the K/V caches to pinned host memory; "
                         "attention then reads only the selected blocks over the host link")
@@ -216,7 +219,7 @@ def main():
         kv_k = msa.HostResident(dev.kcache.cpu().pin_memory())
         kv_v = msa.HostResident(dev.vcache.cpu().pin_memory())
     if decode:
-        run = MSADecode(b, wl.Hkv, wl.G, wl.D, wl.k, P)
+        run = MSADecode(b, wl.Hkv, wl.G, wl.D, wl.k, P, select_mode=args.decode_select)
     elif query_major:
         run = MSAPrefillQueryMajor(b, wl.Hkv, wl.G, wl.D, wl.k, P)
     else:
@@ -230,7 +233,9 @@ def main():
         flush.sum()
 
     # stage boundaries for per-kernel event timing
-    stages = ["score", "select", "attend"] + ([] if decode or query_major else ["merge"])
+    fused_decode = decode and args.decode_select == "attend"
+    stages = (["score", "select_attend"] if fused_decode else
+              ["score", "select", "attend"] + ([] if decode or query_major else ["merge"]))
 
     def step(evs=None):
         for i, name in enumerate(stages):
@@ -242,6 +247,8 @@ def main():
                 run.select()
             elif name == "attend":
                 run.attend(dev.q, kv_k, kv_v, dev.scale)
+            elif name == "select_attend":
+                run.select_attend(dev.q, kv_k, kv_v, dev.scale)
             else:
                 run.merge()
         if evs is not None:
@@ -277,7 +284,7 @@ def main():
 
     # roofline of the scorer (dominant kernel) and of the attention kernel
     score_ms = float(per_stage[:, 0].mean())
-    attend_ms = float(per_stage[:, 2].mean())
+    attend_ms = float(per_stage[:, stages.index("select_attend" if fused_decode else "attend")].mean())
     cand = candidate_tokens(wl)
     if decode:
         sel_tok = selected_tokens(dev, run.sel, run.cnt, union=True)
@@ -286,7 +293,11 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": recorded_traffic(wl.name),
                 "algorithmic_bytes": score_bytes, "avg_ms": score_ms}
         attn_bytes = sel_tok * wl.D * 2 * 2                      # K and V rows of the selected tokens
-        roof_attn = {"kernel": "k_attn_decode+k_merge_splits", "bound": "host link" if kv_on_host else "hbm",
+        if fused_decode:                                         # + the scores the fused top-k reads, once
+            attn_bytes += wl.Nq * wl.Hkv * wl.max_blocks * 4
+        kname = ("msa_topk_attn_decode (top-k, page table, attention)" if fused_decode else "k_attn_decode") + \
+            "+k_merge_splits"
+        roof_attn = {"kernel": kname, "bound": "host link" if kv_on_host else "hbm",
                      "achieved": attn_bytes / (attend_ms * 1e-3) / 1e9,
                      "peak": HOST_LINK_PEAK_GBS if kv_on_host else HBM_PEAK_GBS, "unit": "GB/s",
                      "algorithmic_bytes": attn_bytes, "avg_ms": attend_ms}
@@ -326,7 +337,8 @@ def main():
                    "l2_flush_between_steps": flush is not None,
                    "fused_index_topk": bool(args.fused_topk and not decode),
                    "prefill_mode": None if decode else args.prefill_mode,
-                   "kv_on_host": bool(kv_on_host)},
+                   "kv_on_host": bool(kv_on_host),
+                   "decode_select": args.decode_select if decode else None},
         "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
         "roofline_detail": details,
         "stage_ms": {name: float(per_stage[:, i].mean()) for i, name in enumerate(stages)},

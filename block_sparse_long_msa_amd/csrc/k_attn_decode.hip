@@ -20,6 +20,7 @@
 #include <algorithm>
 
 #include "msa_device.h"
+#include "topk_select.h"
 
 namespace msa {
 
@@ -117,28 +118,40 @@ __device__ __forceinline__ void attend_page(const PageRegs<D>& r, const u32x4 (&
     }
 }
 
-// Workgroup (split s, row rho) attends to the row's pages [s*ppw, (s+1)*ppw) with two pages of
+// LDS of one decode attention workgroup: the four waves' (max, sum, O) for the final combine.
+template <int D>
+struct DecodeLds {
+  static constexpr int OST = D + 4;  // padded row of the per-wave outputs
+  float m[4][16], l[4][16];
+  __align__(16) float o[4][16][OST];
+};
+
+// Page ids of a run read from the row's page table in memory; the first two arrive with the row
+// length, so the first K/V loads wait for one round trip, not two.
+struct PagesInMemory {
+  const int32_t* pt;
+  int j0, pt0, pt1;
+  __device__ int operator()(int j) const { return j == j0 ? pt0 : j == j0 + 1 ? pt1 : pt[j]; }
+};
+// Page ids already on chip (the fused select + attend kernel).
+struct PagesInLds {
+  const int* pt;
+  __device__ int operator()(int j) const { return pt[j]; }
+};
+
+// Workgroup (split sp, row rho) attends to the row's pages [sp*ppw, (sp+1)*ppw) with two pages of
 // loads in flight (one being consumed, the next arriving).  With nsplit = 1 it writes the final
 // bf16 output and LSE; otherwise an fp32 partial and its LSE per (row, split) for the merge.
-template <int D>
-__global__ __launch_bounds__(256, 2) void k_attn_decode(
-    int G, const bf16* __restrict__ q, const bf16* __restrict__ kview, const bf16* __restrict__ vview,
-    int64_t page_stride, int64_t token_stride, const int32_t* __restrict__ page_table, int k,
-    const int32_t* __restrict__ row_len, float scale_log2, int ppw, int nsplit, bf16* __restrict__ out,
-    float* __restrict__ lse_out, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+template <int D, typename Pages>
+__device__ __forceinline__ void attend_run(DecodeLds<D>& sm, int G, const bf16* __restrict__ q,
+                                           const bf16* __restrict__ kview, const bf16* __restrict__ vview,
+                                           int64_t page_stride, int64_t token_stride, const Pages& pages, int len,
+                                           int rho, int sp, int ppw, int nsplit, float scale_log2,
+                                           bf16* __restrict__ out, float* __restrict__ lse_out,
+                                           float* __restrict__ ws_o, float* __restrict__ ws_lse) {
   constexpr int KW = D / 32;
-  constexpr int OST = D + 4;  // padded LDS row of the per-wave outputs
-  __shared__ float sm_m[4][16], sm_l[4][16];
-  __shared__ __align__(16) float sm_o[4][16][OST];
-  const int sp = (int)(blockIdx.x % (unsigned)nsplit), rho = (int)(blockIdx.x / (unsigned)nsplit);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, qd = lane >> 4;
   const int j0 = sp * ppw;
-  const int32_t* pt = page_table + (int64_t)rho * k;
-  // the first two page ids are read together with the row length (both in bounds of the row's k
-  // entries), so the first K/V loads wait for one round trip, not two
-  const int pt0 = pt[j0], pt1 = pt[min(j0 + 1, k - 1)];
-  const int len = row_len[rho];
-  asm volatile("" ::"s"(pt0), "s"(pt1), "s"(len));  // issue the three loads here, side by side
   const int npages = (len + kBlock - 1) / kBlock;
   const int j1 = min(j0 + ppw, npages);
   const int64_t part = (int64_t)rho * nsplit + sp;
@@ -151,8 +164,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
   // and the wait before each page counts exactly the page behind it.
   auto page_valid = [&](int j) { return j < j1 ? min(kBlock, len - j * kBlock) : 1; };
   auto load = [&](PageRegs<D>& r, int j) {
-    const int jc = min(j, j1 - 1);
-    const int64_t vp = jc == j0 ? pt0 : jc == j0 + 1 ? pt1 : pt[jc];
+    const int64_t vp = pages(min(j, j1 - 1));
     load_page<D>(r, kview + vp * page_stride, vview + vp * page_stride, (int)token_stride, page_valid(j), w, n,
                  qd);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute it overlaps
@@ -181,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
   }
 
   // acc[c][ii] = O_w[head n][d = 32qd + 8ii + c] (unnormalized); combine the four waves
-  if (qd == 0) { sm_m[w][n] = m; sm_l[w][n] = l; }
+  if (qd == 0) { sm.m[w][n] = m; sm.l[w][n] = l; }
   if (n < G) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
@@ -189,8 +201,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
       if (d < D) {
         const f32x4 lo = {acc[0][ii], acc[1][ii], acc[2][ii], acc[3][ii]};
         const f32x4 hi = {acc[4][ii], acc[5][ii], acc[6][ii], acc[7][ii]};
-        *reinterpret_cast<f32x4*>(&sm_o[w][n][d]) = lo;
-        *reinterpret_cast<f32x4*>(&sm_o[w][n][d + 4]) = hi;
+        *reinterpret_cast<f32x4*>(&sm.o[w][n][d]) = lo;
+        *reinterpret_cast<f32x4*>(&sm.o[w][n][d + 4]) = hi;
       }
     }
   }
@@ -199,15 +211,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
     const int h = (4 * e) / D, d = (4 * e) % D;
     float M = neg_inf();
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm_m[ww][h]);
+    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sm.m[ww][h]);
     float den = 0.f;
     f32x4 o = fzero4();
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      const float mw = sm_m[ww][h];
+      const float mw = sm.m[ww][h];
       const float f = (mw == neg_inf()) ? 0.f : fast_exp2(mw - M);
-      den += f * sm_l[ww][h];
-      const f32x4 x = *reinterpret_cast<const f32x4*>(&sm_o[ww][h][d]);
+      den += f * sm.l[ww][h];
+      const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.o[ww][h][d]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) o[t] += f * x[t];
     }
@@ -225,6 +237,91 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
       if (d == 0) ws_lse[part * G + h] = lse;
     }
   }
+}
+
+// Decode attention over a page table in memory: workgroup (split, row) = blockIdx.x as (rho*nsplit + sp).
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_attn_decode(
+    int G, const bf16* __restrict__ q, const bf16* __restrict__ kview, const bf16* __restrict__ vview,
+    int64_t page_stride, int64_t token_stride, const int32_t* __restrict__ page_table, int k,
+    const int32_t* __restrict__ row_len, float scale_log2, int ppw, int nsplit, bf16* __restrict__ out,
+    float* __restrict__ lse_out, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+  __shared__ DecodeLds<D> sm;
+  const int sp = (int)(blockIdx.x % (unsigned)nsplit), rho = (int)(blockIdx.x / (unsigned)nsplit);
+  const int j0 = sp * ppw;
+  const int32_t* pt = page_table + (int64_t)rho * k;
+  // the first two page ids are read together with the row length (both in bounds of the row's k
+  // entries), so the first K/V loads wait for one round trip, not two
+  const int pt0 = pt[j0], pt1 = pt[min(j0 + 1, k - 1)];
+  const int len = row_len[rho];
+  asm volatile("" ::"s"(pt0), "s"(pt1), "s"(len));  // issue the three loads here, side by side
+  const PagesInMemory pages{pt, j0, pt0, pt1};
+  attend_run<D>(sm, G, q, kview, vview, page_stride, token_stride, pages, len, rho, sp, ppw, nsplit, scale_log2,
+                out, lse_out, ws_o, ws_lse);
+}
+
+// Top-k, page table and decode attention in one launch.  Workgroup (split sp, row rho) selects its
+// row's blocks itself -- the same row_topk as the top-k kernel, over the row's scores in registers
+// of its four waves -- with the block table entries of all candidate ids read beside the scores, so
+// the page ids of the chosen blocks are on chip as soon as the selection is.  Split 0 also writes
+// the row's selection, count, page table and row length; then every split attends to its run of
+// pages exactly as k_attn_decode does.  The row's few hundred scores are read by each of its splits
+// instead of once, which costs far less than the launch and the page-table round trip it saves.
+// Caches [pages, 128, Hkv, D]: the view of KV head g has page stride D and token stride Hkv*D, and
+// the virtual page of physical page p is p*128*Hkv + g.
+template <int D, int R>  // R scores per thread: max_blocks <= 256*R
+__global__ __launch_bounds__(256, 2) void k_select_attend(
+    int B, int Hkv, int max_blocks, const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_len,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int k,
+    int32_t* __restrict__ sel, int32_t* __restrict__ cnt, int32_t* __restrict__ page_table,
+    int32_t* __restrict__ row_len, int G, const bf16* __restrict__ q, const bf16* __restrict__ kcache,
+    const bf16* __restrict__ vcache, float scale_log2, int ppw, int nsplit, bf16* __restrict__ out,
+    float* __restrict__ lse_out, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+  constexpr int NW = 4, NT = 256;
+  __shared__ DecodeLds<D> sm;
+  __shared__ RowTopkLds<NW> sh;
+  __shared__ int s_sel[64], s_pt[64], s_len;
+  const int sp = (int)(blockIdx.x % (unsigned)nsplit), rho = (int)(blockIdx.x / (unsigned)nsplit);
+  const int t = rho / Hkv, g = rho - t * Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int pos = q_pos[t];
+  const int n = min(pos / kBlock + 1, max_blocks);
+  const float* srow = scores + (int64_t)rho * max_blocks;
+  float v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] = srow[min(tid + NT * r, max_blocks - 1)];
+  int r_req, L;
+  request_and_len(cu_q, ctx_len, B, t, r_req, L);
+  const int lim = min(pos + 1, L);  // tokens s < lim are valid
+  int bt[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) bt[r] = block_table[(int64_t)r_req * max_blocks + min(tid + NT * r, max_blocks - 1)];
+
+  const int c = row_topk<NW, R>(v, n, k, sh, [&](int slot, int id, int r) {
+    s_sel[slot] = id;
+    s_pt[slot] = bt[r] * (kBlock * Hkv) + g;
+  });
+  __syncthreads();
+  if (wv == 0) {
+    int len = lane < c ? min(kBlock, lim - s_sel[lane] * kBlock) : 0;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) len += __shfl_xor(len, m, kWave);
+    if (lane == 0) s_len = len;
+    if (sp == 0) {
+      if (lane < k) {
+        sel[(int64_t)rho * k + lane] = lane < c ? s_sel[lane] : -1;
+        page_table[(int64_t)rho * k + lane] = lane < c ? s_pt[lane] : -1;
+      }
+      if (lane == 0) {
+        cnt[rho] = c;
+        row_len[rho] = len;
+      }
+    }
+  }
+  __syncthreads();
+  const PagesInLds pages{s_pt};
+  attend_run<D>(sm, G, q, kcache, vcache, D, (int64_t)Hkv * D, pages, s_len, rho, sp, ppw, nsplit, scale_log2, out,
+                lse_out, ws_o, ws_lse);
 }
 
 // Merge of the decode splits: one workgroup per (row, head).  Thread (g, c) folds the parts
@@ -389,6 +486,16 @@ int decode_splits(int rows, int k) {
   return (k + ppw - 1) / ppw;
 }
 
+static hipError_t launch_merge_splits(int rows, int G, int D, int nsplit, const float* ws_o, const float* ws_lse,
+                                      bf16* out, float* lse, hipStream_t stream) {
+  const dim3 mgrid((unsigned)((int64_t)rows * G));
+  if (D == 128)
+    hipLaunchKernelGGL(k_merge_splits<128>, mgrid, dim3(256), 0, stream, nsplit, G, ws_o, ws_lse, out, lse);
+  else
+    hipLaunchKernelGGL(k_merge_splits<64>, mgrid, dim3(256), 0, stream, nsplit, G, ws_o, ws_lse, out, lse);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_decode(int rows, int G, int D, const void* q, const void* kview, const void* vview,
                               int64_t page_stride, int64_t token_stride, const int32_t* page_table, int k,
                               const int32_t* row_len, float sm_scale, void* out, float* lse, float* ws_o,
@@ -409,12 +516,50 @@ hipError_t launch_attn_decode(int rows, int G, int D, const void* q, const void*
                        page_table, k, row_len, sl2, ppw, nsplit, oo, lse, ws_o, ws_lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
-  const dim3 mgrid((unsigned)((int64_t)rows * G));
-  if (D == 128)
-    hipLaunchKernelGGL(k_merge_splits<128>, mgrid, dim3(256), 0, stream, nsplit, G, ws_o, ws_lse, oo, lse);
-  else
-    hipLaunchKernelGGL(k_merge_splits<64>, mgrid, dim3(256), 0, stream, nsplit, G, ws_o, ws_lse, oo, lse);
-  return hipGetLastError();
+  return launch_merge_splits(rows, G, D, nsplit, ws_o, ws_lse, oo, lse, stream);
+}
+
+// Beyond 4096 blocks per row the selection repeated by every split of a row costs as much as the
+// separate top-k kernel (measured on million-token rows), so those rows keep the two launches.
+int select_attend_max_blocks() { return 256 * 16; }
+
+// Top-k + page table + decode attention in one launch (plus the split merge); max_blocks must be
+// at most select_attend_max_blocks().  Same splits, pages and arithmetic as the separate calls.
+hipError_t launch_select_attend(int B, int Nq, int Hkv, int max_blocks, const int32_t* block_table,
+                                const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const float* scores,
+                                int k, int32_t* sel, int32_t* cnt, int32_t* page_table, int32_t* row_len, int G, int D,
+                                const void* q, const void* kcache, const void* vcache, float sm_scale, void* out,
+                                float* lse, float* ws_o, float* ws_lse, hipStream_t stream) {
+  const int rows = Nq * Hkv;
+  const int nsplit = decode_splits(rows, k);
+  const int ppw = (k + nsplit - 1) / nsplit;
+  const dim3 grid((unsigned)((int64_t)nsplit * rows)), block(256);
+  const float sl2 = sm_scale * kLog2e;
+  const bf16* qq = static_cast<const bf16*>(q);
+  const bf16* kc = static_cast<const bf16*>(kcache);
+  const bf16* vc = static_cast<const bf16*>(vcache);
+  bf16* oo = static_cast<bf16*>(out);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, stream, B, Hkv, max_blocks, block_table, ctx_len, cu_q, q_pos, scores, k,
+                       sel, cnt, page_table, row_len, G, qq, kc, vc, sl2, ppw, nsplit, oo, lse, ws_o, ws_lse);
+  };
+  const int r = max_blocks <= 256 ? 1 : max_blocks <= 512 ? 2 : max_blocks <= 1024 ? 4 : max_blocks <= 2048 ? 8 : 16;
+  if (D == 128) {
+    if (r == 1) go(k_select_attend<128, 1>);
+    else if (r == 2) go(k_select_attend<128, 2>);
+    else if (r == 4) go(k_select_attend<128, 4>);
+    else if (r == 8) go(k_select_attend<128, 8>);
+    else go(k_select_attend<128, 16>);
+  } else {
+    if (r == 1) go(k_select_attend<64, 1>);
+    else if (r == 2) go(k_select_attend<64, 2>);
+    else if (r == 4) go(k_select_attend<64, 4>);
+    else if (r == 8) go(k_select_attend<64, 8>);
+    else go(k_select_attend<64, 16>);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  return launch_merge_splits(rows, G, D, nsplit, ws_o, ws_lse, oo, lse, stream);
 }
 
 hipError_t launch_lse_merge_bf16(int64_t rows, int parts, int G, int D, const void* part_o, const float* part_lse,

@@ -13,6 +13,7 @@
 #include <type_traits>
 
 #include "msa_device.h"
+#include "topk_select.h"
 
 namespace msa {
 
@@ -154,11 +155,9 @@ __global__ __launch_bounds__(64 * NW) void k_topk(int B, int Hkv, int max_blocks
 }
 
 // The same selection for rows whose candidates fit in registers (64*NW*R >= n): every lane
-// reads its R scores once, and the k-th largest key T is found bit by bit from the highest bit
-// the keys do not all share, counting the keys at or above each trial threshold with ballots.
-// T is the largest value with at least k keys >= T, so fewer than k keys are > T and the
-// boundary ties are taken in id order exactly as above.  Against the radix passes it saves the
-// re-reads of the scores and the LDS histogram round trips.
+// reads its R scores once and row_topk (topk_select.h) finds the k-th largest key bit by bit with
+// ballot counts.  Against the radix passes it saves the re-reads of the scores and the LDS
+// histogram round trips.
 //
 // With page_table != NULL the same launch also writes the row's decode page table and row length
 // (as k_page_table below), from the chosen ids kept in LDS; the request lookup is issued at the
@@ -178,8 +177,7 @@ __global__ __launch_bounds__(64 * NW) void k_topk_reg(int Hkv, int max_blocks, c
                                                       int32_t* __restrict__ sel, int32_t* __restrict__ cnt,
                                                       PageTableOut pto) {
   constexpr int NT = 64 * NW;
-  __shared__ uint32_t s_c[2][NW];
-  __shared__ uint32_t s_r[2][NW];
+  __shared__ RowTopkLds<NW> sh;
   __shared__ int s_sel[64];
   const int row = blockIdx.x;  // t*Hkv + g
   const int t = row / Hkv;
@@ -201,129 +199,29 @@ __global__ __launch_bounds__(64 * NW) void k_topk_reg(int Hkv, int max_blocks, c
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) asm volatile("" ::"v"(v[r]));
-  // the chosen ids in ascending order, c of them, also kept in s_sel[0 .. c-1]
-  auto page_table = [&](int c) {
+
+  const int c = row_topk<NW, R>(v, n, k, sh, [&](int slot, int id, int) {
+    out[slot] = id;
+    s_sel[slot] = id;
+  });
+  for (int i = c + tid; i < k; i += NT) out[i] = -1;
+  if (tid == 0) cnt[row] = c;
+  if (pto.page_table) {  // the chosen ids, in ascending order, are in s_sel[0 .. c-1]
     __syncthreads();
     if (wv == 0) {
       const int g = row - t * Hkv;
-      int v = -1, len = 0;
+      int pv = -1, len = 0;
       if (lane < c) {
         const int bl = s_sel[lane];
-        v = pto.block_table[(int64_t)r_req * max_blocks + bl] * (kBlock * Hkv) + g;
+        pv = pto.block_table[(int64_t)r_req * max_blocks + bl] * (kBlock * Hkv) + g;
         len = min(kBlock, lim - bl * kBlock);
       }
-      if (lane < k) pto.page_table[(int64_t)row * k + lane] = v;
+      if (lane < k) pto.page_table[(int64_t)row * k + lane] = pv;
 #pragma unroll
       for (int m = 1; m < kWave; m <<= 1) len += __shfl_xor(len, m, kWave);
       if (lane == 0) pto.row_len[row] = len;
     }
-  };
-  if (n <= k) {
-    for (int i = tid; i < k; i += NT) {
-      out[i] = i < n ? i : -1;
-      s_sel[i] = i;
-    }
-    if (tid == 0) cnt[row] = n;
-    if (pto.page_table) page_table(n);
-    return;
   }
-  // ids >= n get key 0, below every candidate key (candidate scores are finite)
-  uint32_t key[R];
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const bool in = tid + NT * r < n;
-    const uint32_t kr = order_key(v[r]);
-    key[r] = in ? kr : 0u;
-    kmin = min(kmin, in ? kr : 0xffffffffu);
-    kmax = max(kmax, key[r]);
-  }
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, m, kWave));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m, kWave));
-  }
-  if (NW > 1) {
-    if (lane == 0) { s_r[0][wv] = kmin; s_r[1][wv] = kmax; }
-    __syncthreads();
-    for (int x = 0; x < NW; ++x) { kmin = min(kmin, s_r[0][x]); kmax = max(kmax, s_r[1][x]); }
-  }
-  // counts of keys >= thr over the whole row (uniform result)
-  auto count_ge = [&](uint32_t thr, int parity) -> int {
-    int c = 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) c += __popcll(__ballot(key[r] >= thr));
-    if (NW > 1) {
-      if (lane == 0) s_c[parity][wv] = c;
-      __syncthreads();
-      c = 0;
-      for (int x = 0; x < NW; ++x) c += s_c[parity][x];
-    }
-    return c;
-  };
-  // T: the largest threshold with at least k keys >= T found so far.  The search stops early once
-  // exactly k keys are >= T: those are the top k, whatever T's low bits (with a tie across the
-  // boundary it runs down to bit 0 and T is the k-th largest key).
-  uint32_t T = kmin;
-  int parity = 0;  // buffer of the next count (alternates, so a slow wave's read is never overwritten)
-  if (kmin != kmax) {
-    const int hb = 31 - __builtin_clz(kmin ^ kmax);
-    T = hb == 31 ? 0u : (kmin & ~((2u << hb) - 1u));
-    for (int b = hb; b >= 0; --b) {  // every trial threshold is >= 1, so id slots past n never count
-      const uint32_t cand = T | (1u << b);
-      const int c = count_ge(cand, parity);
-      parity ^= 1;
-      if (c >= k) {
-        T = cand;
-        if (c == k) break;
-      }
-    }
-  }
-  const int remaining = k - (T == 0xffffffffu ? 0 : count_ge(T + 1u, parity));
-
-  // emit in id order: keys above T, then the first `remaining` keys equal to T
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int written = 0, ties_seen = 0;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int i = tid + NT * r;
-    const bool gt = key[r] > T;
-    const bool eq = i < n && key[r] == T;
-    const uint64_t eqm = __ballot(eq);
-    int eq_before = ties_seen + __popcll(eqm & lt_mask);
-    int eq_all = __popcll(eqm);
-    if (NW > 1) {
-      __syncthreads();  // s_c of the previous use is read by every wave
-      if (lane == 0) s_c[0][wv] = eq_all;
-      __syncthreads();
-      eq_all = 0;
-      for (int x = 0; x < NW; ++x) {
-        if (x < wv) eq_before += s_c[0][x];
-        eq_all += s_c[0][x];
-      }
-    }
-    const bool take = gt || (eq && eq_before < remaining);
-    const uint64_t tm = __ballot(take);
-    int slot = written + __popcll(tm & lt_mask);
-    int take_all = __popcll(tm);
-    if (NW > 1) {
-      if (lane == 0) s_c[1][wv] = take_all;
-      __syncthreads();
-      take_all = 0;
-      for (int x = 0; x < NW; ++x) {
-        if (x < wv) slot += s_c[1][x];
-        take_all += s_c[1][x];
-      }
-    }
-    if (take && slot < k) {
-      out[slot] = i;
-      s_sel[slot] = i;
-    }
-    written += take_all;
-    ties_seen += eq_all;
-  }
-  if (tid == 0) cnt[row] = k;
-  if (pto.page_table) page_table(k);
 }
 
 // Decode sparse page table over the strided view (Chinese page, section "MSA需要新的分页注意力集成"):

@@ -30,6 +30,12 @@ hipError_t launch_topk_page_table(int B, int Nq, int Hkv, int max_blocks, const 
                                   const float* scores, int k, int32_t* sel, int32_t* cnt, int32_t* page_table,
                                   int32_t* row_len, hipStream_t stream);
 int decode_splits(int rows, int k);
+int select_attend_max_blocks();
+hipError_t launch_select_attend(int B, int Nq, int Hkv, int max_blocks, const int32_t* block_table,
+                                const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const float* scores,
+                                int k, int32_t* sel, int32_t* cnt, int32_t* page_table, int32_t* row_len, int G, int D,
+                                const void* q, const void* kcache, const void* vcache, float sm_scale, void* out,
+                                float* lse, float* ws_o, float* ws_lse, hipStream_t stream);
 hipError_t launch_attn_decode(int rows, int G, int D, const void* q, const void* kview, const void* vview,
                               int64_t page_stride, int64_t token_stride, const int32_t* page_table, int k,
                               const int32_t* row_len, float sm_scale, void* out, float* lse, float* ws_o,
@@ -289,6 +295,57 @@ msa_status msa_sparse_attn_decode(int32_t rows, int32_t G, int32_t D, const void
   return from_hip(msa::launch_attn_decode(rows, G, D, q, k_base, v_base, page_stride, token_stride, page_table, k,
                                           row_len, sm_scale, out, lse, ws_o, ws_lse, st),
                   "msa_sparse_attn_decode launch");
+}
+
+msa_status msa_topk_attn_decode(const msa_batch* batch, const float* scores, int32_t k, msa_cache k_cache,
+                                msa_cache v_cache, int32_t G, const void* q, float sm_scale, int32_t* sel, int32_t* cnt,
+                                int32_t* page_table, int32_t* row_len, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, msa_stream_t stream) {
+  g_last_error.clear();
+  if (msa_status s = check_batch(batch)) return s;
+  if (msa_status s = check_cache(k_cache, "k_cache")) return s;
+  if (msa_status s = check_cache(v_cache, "v_cache")) return s;
+  MSA_REQUIRE(k_cache.num_pages == v_cache.num_pages && k_cache.num_heads == v_cache.num_heads &&
+                  k_cache.head_dim == v_cache.head_dim,
+              MSA_ERR_INVALID_ARG, "k_cache and v_cache must have the same shape");
+  const int Hkv = k_cache.num_heads, D = k_cache.head_dim;
+  MSA_REQUIRE(supported_group(G), MSA_ERR_UNSUPPORTED, "G must be 1, 2, 4, 8 or 16, got %d", G);
+  MSA_REQUIRE(k >= 1 && k <= kMaxK, MSA_ERR_UNSUPPORTED, "k must be in [1, %d], got %d", kMaxK, k);
+  MSA_REQUIRE((int64_t)k_cache.num_pages * 128 * Hkv <= 0x7fffffffLL, MSA_ERR_UNSUPPORTED,
+              "num_pages*128*num_heads must fit in int32 (virtual page ids)");
+  const int64_t rows64 = (int64_t)batch->num_queries * Hkv;
+  MSA_REQUIRE(rows64 * k <= 0x7fffffffLL, MSA_ERR_UNSUPPORTED, "num_queries*num_heads*k must fit in int32");
+  if (batch->num_queries == 0) return MSA_OK;
+  MSA_REQUIRE(scores && q && sel && cnt && page_table && row_len && out, MSA_ERR_INVALID_ARG,
+              "scores, q, sel, cnt, page_table, row_len and out must be non-NULL");
+  MSA_REQUIRE(aligned16(q) && aligned16(out) && aligned16(workspace), MSA_ERR_INVALID_ARG,
+              "q, out and workspace must be 16-byte aligned");
+  MSA_REQUIRE(aligned4(scores) && aligned4(sel) && aligned4(cnt) && aligned4(page_table) && aligned4(row_len) &&
+                  aligned4(lse),
+              MSA_ERR_INVALID_ARG, "scores, sel, cnt, page_table, row_len and lse must be 4-byte aligned");
+  const int rows = (int)rows64;
+  const size_t need = msa_sparse_attn_decode_workspace_size(rows, G, D, k);
+  MSA_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), MSA_ERR_WORKSPACE_TOO_SMALL,
+              "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  const size_t parts = (size_t)rows * msa::decode_splits(rows, k) * G;
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_lse = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(parts * D * sizeof(float)))
+                       : nullptr;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (batch->max_blocks <= msa::select_attend_max_blocks())
+    return from_hip(msa::launch_select_attend(batch->num_requests, batch->num_queries, Hkv, batch->max_blocks,
+                                              batch->block_table, batch->ctx_len, batch->cu_q, batch->q_pos, scores,
+                                              k, sel, cnt, page_table, row_len, G, D, q, k_cache.data, v_cache.data,
+                                              sm_scale, out, lse, ws_o, ws_lse, st),
+                    "msa_topk_attn_decode launch");
+  // rows too long to select inside the attention workgroup: the two launches of the separate calls
+  hipError_t e = msa::launch_topk_page_table(batch->num_requests, batch->num_queries, Hkv, batch->max_blocks,
+                                             batch->block_table, batch->ctx_len, batch->cu_q, batch->q_pos, scores, k,
+                                             sel, cnt, page_table, row_len, st);
+  if (e != hipSuccess) return from_hip(e, "msa_topk_attn_decode top-k launch");
+  return from_hip(msa::launch_attn_decode(rows, G, D, q, k_cache.data, v_cache.data, D, (int64_t)Hkv * D, page_table,
+                                          k, row_len, sm_scale, out, lse, ws_o, ws_lse, st),
+                  "msa_topk_attn_decode attention launch");
 }
 
 size_t msa_sparse_attn_prefill_workspace_size(const msa_batch* batch, int32_t num_kv_heads, int32_t k) {

@@ -1,7 +1,7 @@
 """One MSA layer invocation as a chain of C-ABI calls with preallocated buffers.
 
-MSADecode: index scores -> top-k + sparse page table -> decode attention (split over pages,
-           merged in the library).
+MSADecode: index scores -> top-k + sparse page table + decode attention (split over pages,
+           merged in the library), by default in one call after the scores.
 MSAPrefill: index scores -> top-k -> KV-block-major attention (partials) -> LSE merge.
 MSAPrefillQueryMajor: the query-major baseline the KV-block-major mapping is measured against:
            index scores -> top-k + page table -> every (query token, KV head) row attends to its own
@@ -15,19 +15,26 @@ import torch
 
 from . import (Batch, msa_build_sparse_page_table, msa_index_score, msa_index_topk, msa_index_topk_workspace_size,
                msa_lse_merge, msa_sparse_attn_decode, msa_sparse_attn_decode_workspace_size,
-               msa_sparse_attn_prefill, msa_sparse_attn_prefill_workspace_size, msa_topk_blocks,
-               msa_topk_page_table)
+               msa_sparse_attn_prefill, msa_sparse_attn_prefill_workspace_size, msa_topk_attn_decode,
+               msa_topk_blocks, msa_topk_page_table)
 
 
 class MSADecode:
-    """``fused_select`` (default) runs top-k and the page table as one call (msa_topk_page_table);
-    ``False`` runs msa_topk_blocks and msa_build_sparse_page_table.  Both give identical results."""
+    """``select_mode`` picks how the blocks are selected and attended after the scores:
+    "attend" (default): msa_topk_attn_decode, top-k + page table + attention in one launch;
+    "page_table": msa_topk_page_table, then msa_sparse_attn_decode;
+    "separate": msa_topk_blocks, msa_build_sparse_page_table, then msa_sparse_attn_decode.
+    All three give bit-identical results and fill the same buffers."""
+
+    MODES = ("attend", "page_table", "separate")
 
     def __init__(self, batch: Batch, Hkv: int, G: int, D: int, k: int, num_pages: int, device="cuda",
-                 fused_select: bool = True):
+                 select_mode: str = "attend"):
+        if select_mode not in self.MODES:
+            raise ValueError(f"select_mode must be one of {self.MODES}, got {select_mode!r}")
         Nq, mb = batch.num_queries, batch.max_blocks
         self.batch, self.Hkv, self.G, self.D, self.k, self.num_pages = batch, Hkv, G, D, k, num_pages
-        self.fused_select = fused_select
+        self.select_mode = select_mode
         self.rows = Nq * Hkv
         self.scores = torch.empty((Nq, Hkv, mb), dtype=torch.float32, device=device)
         self.sel = torch.empty((Nq, Hkv, k), dtype=torch.int32, device=device)
@@ -43,22 +50,32 @@ class MSADecode:
         msa_index_score(self.batch, q_idx, kidx, self.scores, stream)
 
     def select(self, stream=None):
-        if self.fused_select:
-            msa_topk_page_table(self.batch, self.Hkv, self.num_pages, self.scores, self.k, self.sel, self.cnt,
-                                self.page_table, self.row_len, stream)
-        else:
+        """Top-k and page table only (the "page_table" and "separate" modes)."""
+        if self.select_mode == "separate":
             msa_topk_blocks(self.batch, self.Hkv, self.scores, self.k, self.sel, self.cnt, stream)
             msa_build_sparse_page_table(self.batch, self.Hkv, self.num_pages, self.sel, self.cnt, self.k,
                                         self.page_table, self.row_len, stream)
+        else:
+            msa_topk_page_table(self.batch, self.Hkv, self.num_pages, self.scores, self.k, self.sel, self.cnt,
+                                self.page_table, self.row_len, stream)
 
     def attend(self, q, kcache, vcache, sm_scale: float, stream=None):
+        """Decode attention over the page table written by select()."""
         msa_sparse_attn_decode(self.rows, self.G, self.D, q, kcache, vcache, self.D, self.Hkv * self.D,
                                self.page_table, self.k, self.row_len, sm_scale, self.out, self.lse, self.ws, stream)
 
+    def select_attend(self, q, kcache, vcache, sm_scale: float, stream=None):
+        """Top-k, page table and attention from the scores, in the way ``select_mode`` says."""
+        if self.select_mode == "attend":
+            msa_topk_attn_decode(self.batch, self.scores, self.k, kcache, vcache, self.G, q, sm_scale, self.sel,
+                                 self.cnt, self.page_table, self.row_len, self.out, self.lse, self.ws, stream)
+        else:
+            self.select(stream)
+            self.attend(q, kcache, vcache, sm_scale, stream)
+
     def __call__(self, q, q_idx, kcache, vcache, kidx, sm_scale: float, stream=None):
         self.score(q_idx, kidx, stream)
-        self.select(stream)
-        self.attend(q, kcache, vcache, sm_scale, stream)
+        self.select_attend(q, kcache, vcache, sm_scale, stream)
         return self.out, self.lse
 
 

@@ -155,6 +155,23 @@ msa_status msa_sparse_attn_decode(int32_t rows, int32_t G, int32_t D, const void
                                   size_t workspace_bytes, msa_stream_t stream);
 size_t msa_sparse_attn_decode_workspace_size(int32_t rows, int32_t G, int32_t D, int32_t k);
 
+/* msa_topk_page_table followed by msa_sparse_attn_decode on the caches' per-KV-head strided views,
+ * in one launch (plus the split merge).  Each attention workgroup selects its row's blocks itself,
+ * so the page table never makes a round trip through memory before attention starts; the pages name
+ * handing the top-k to decode attention on chip as open work for MSA's small kernels (Chinese page,
+ * section "遗留问题"; Japanese page, "今後の取り組み").  Outputs and results are identical to the
+ * two calls: sel, cnt, page_table and row_len as msa_topk_page_table (all four are written), out and
+ * lse as msa_sparse_attn_decode with rows = Nq*Hkv, page stride D and token stride Hkv*D.  Rows of
+ * more than 4096 blocks (batch->max_blocks) run the two calls' launches instead.
+ *   scores            device f32 [Nq, Hkv, max_blocks] as written by msa_index_score
+ *   k_cache, v_cache  [pages, 128, Hkv, D]
+ *   q                 device bf16 [Nq, Hkv*G, D];  out  device bf16 [Nq, Hkv*G, D];  lse  f32 [Nq, Hkv*G] or NULL
+ *   workspace         device, >= msa_sparse_attn_decode_workspace_size(Nq*Hkv, G, D, k) bytes */
+msa_status msa_topk_attn_decode(const msa_batch* batch, const float* scores, int32_t k, msa_cache k_cache,
+                                msa_cache v_cache, int32_t G, const void* q, float sm_scale, int32_t* sel,
+                                int32_t* cnt, int32_t* page_table, int32_t* row_len, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, msa_stream_t stream);
+
 /* KV-block-major prefill attention (section "KV块主序稀疏注意力减少冗余KV移动"; Russian page,
  * third paragraph): the selection is inverted into {(KV head, physical page) -> queries}
  * lists, each selected KV block is staged on chip and attended by every query row that

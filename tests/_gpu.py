@@ -96,6 +96,23 @@ def decode_attention(dev, pt, rl, k=None):
     return out, lse
 
 
+def topk_attn_decode(dev, b, s, k=None):
+    """msa_topk_attn_decode: top-k, page table and decode attention in one call.  Returns
+    (sel, cnt, page_table, row_len, out, lse), every buffer poisoned beforehand."""
+    wl = dev.wl
+    k = k or wl.k
+    msa = lib()
+    rows = wl.Nq * wl.Hkv
+    sel, cnt = poison_i32(wl.Nq, wl.Hkv, k), poison_i32(wl.Nq, wl.Hkv)
+    pt, rl = poison_i32(rows, k), poison_i32(rows)
+    out = torch.full((wl.Nq, wl.Hq, wl.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = nan_f32(wl.Nq, wl.Hq)
+    ws = torch.empty(msa.msa_sparse_attn_decode_workspace_size(rows, wl.G, wl.D, k), dtype=torch.uint8,
+                     device="cuda")
+    msa.msa_topk_attn_decode(b, s, k, dev.kcache, dev.vcache, wl.G, dev.q, dev.scale, sel, cnt, pt, rl, out, lse, ws)
+    return sel, cnt, pt, rl, out, lse
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     torch.cuda.synchronize()
     if t.dtype == torch.bfloat16:

@@ -125,6 +125,30 @@ def test_decode_attention_rejects(lib, G, D, ps, ts, k, ws, status):
 
 
 @no_gpu
+@pytest.mark.parametrize("G,k,kc,vc,ws,status", [
+    (3, 16, dict(), dict(), 1 << 30, UNSUPPORTED),                  # G not a power of two <= 16
+    (8, 0, dict(), dict(), 1 << 30, UNSUPPORTED),
+    (8, 65, dict(), dict(), 1 << 30, UNSUPPORTED),
+    (8, 16, dict(), dict(D=128), 1 << 30, INVALID),                 # K and V caches differ
+    (8, 16, dict(H=8, P=1 << 22), dict(H=8, P=1 << 22), 1 << 30, UNSUPPORTED),   # virtual page ids beyond int32
+    (8, 16, dict(BS=64), dict(BS=64), 1 << 30, UNSUPPORTED),
+    (8, 16, dict(), dict(), 64, WS_SMALL),                          # 4 rows are split: a workspace is needed
+])
+def test_topk_attn_decode_rejects(lib, G, k, kc, vc, ws, status):
+    b = _batch()
+    st = lib.msa_topk_attn_decode(ctypes.byref(b), FAKE, k, _cache(**kc), _cache(**vc), G, FAKE, 0.1, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, FAKE, ws, None)
+    assert st == status
+
+
+@no_gpu
+def test_topk_attn_decode_rejects_null_outputs(lib):
+    b = _batch()
+    assert lib.msa_topk_attn_decode(ctypes.byref(b), FAKE, 4, _cache(), _cache(), 8, FAKE, 0.1, FAKE, FAKE, None,
+                                    FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == INVALID
+
+
+@no_gpu
 def test_prefill_attention_rejects(lib):
     b = _batch(Nq=40, maxq=40)
     kc, vc = _cache(), _cache()
@@ -148,6 +172,8 @@ def test_empty_inputs_launch_nothing(lib):
     assert lib.msa_index_score(ctypes.byref(b), None, _cache(), None, None) == OK
     assert lib.msa_topk_blocks(ctypes.byref(b), 2, None, 4, None, None, None) == OK
     assert lib.msa_topk_page_table(ctypes.byref(b), 2, 8, None, 4, None, None, None, None, None) == OK
+    assert lib.msa_topk_attn_decode(ctypes.byref(b), None, 4, _cache(), _cache(), 8, None, 0.1, None, None, None,
+                                    None, None, None, None, 0, None) == OK
     assert lib.msa_lse_merge(0, 4, 8, 128, None, None, None, None, None) == OK
     assert lib.msa_sparse_attn_decode(0, 8, 128, None, None, None, 128, 1024, None, 4, None, 0.1, None, None, None,
                                       0, None) == OK

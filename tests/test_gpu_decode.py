@@ -12,7 +12,8 @@ import torch
 
 import msa_inputs as mi
 import oracle
-from _gpu import announce, batch, decode_attention, host, lib, page_table, scores, setup, topk, topk_page_table
+from _gpu import (announce, batch, decode_attention, host, lib, page_table, scores, setup, topk, topk_attn_decode,
+                  topk_page_table)
 from _helpers import assert_attn_close, np_inputs, selection_excused
 
 pytestmark = pytest.mark.gpu
@@ -59,6 +60,9 @@ def _run(dev, max_q=None):
     for a, f in zip((sel, cnt, pt, rl), topk_page_table(dev, b, s)):
         assert torch.equal(a, f), "msa_topk_page_table differs from msa_topk_blocks + msa_build_sparse_page_table"
     out, lse = decode_attention(dev, pt, rl)
+    # top-k, page table and attention in one call: the same six arrays bit for bit
+    for a, f in zip((sel, cnt, pt, rl, out, lse), topk_attn_decode(dev, b, s)):
+        assert torch.equal(a, f), "msa_topk_attn_decode differs from the separate calls"
     return s, sel, cnt, pt, rl, out, lse
 
 
