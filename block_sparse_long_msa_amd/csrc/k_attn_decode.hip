@@ -15,6 +15,9 @@
 //   64-byte segments.  The four waves' (max, sum, O) are combined through LDS.  A row is split
 //   over several workgroups only as far as needed to occupy the chip; the splits are then
 //   combined by k_merge_splits.
+// k_select_attend: the top-k, the page table and k_attn_decode in one launch -- each attention
+//   workgroup selects its own row's blocks from the scores (row_topk, topk_select.h) and takes the
+//   chosen pages' ids from LDS instead of a page table in memory.
 // k_lse_merge: LSE = log sum_j exp(lse_j); O = sum_j exp(lse_j - LSE) O_j over the parts with
 //   lse_j > -inf (section "KV块主序稀疏注意力减少冗余KV移动").
 #include <algorithm>

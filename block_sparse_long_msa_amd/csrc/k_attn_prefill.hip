@@ -6,13 +6,11 @@
 // it, and because a block only yields a partial output, a log-sum-exp reduction rescales and
 // sums the partials afterwards (k_lse_merge).
 //
-// Remap (a counting sort, three tiny kernels):
-//   bucket = (KV head g, request r, logical block b), ordered g-major so the query rows of one
-//   KV head (the operand re-read once per selected block) stay resident in the MALL while that
-//   head's buckets run.  count -> exclusive scan -> scatter (t, j) into the bucket lists, plus a
-//   work list of (bucket, chunk of kChunk query tokens).  Order within a bucket is not fixed,
-//   but every (t, g, j) result is computed from its own query row only, so outputs are exact
-//   and reproducible whatever the order.
+// Remap (a counting sort):
+//   bucket = (KV head g, request r, logical block b), ordered g-major.  count -> exclusive scan
+//   -> scatter (t, j) into the bucket lists, plus a work list of (bucket, chunk of kChunk query
+//   tokens).  Order within a bucket is not fixed, but every (t, g, j) result is computed from its
+//   own query row only, so outputs are exact and reproducible whatever the order.
 //
 // k_attn_kvbm: one workgroup per work item.  It stages block b of KV head g in LDS once -- K
 // row-major and V transposed -- then streams the chunk's query rows through it in passes of
@@ -24,7 +22,8 @@
 // gets its normalized partial output (bf16) and natural-log LSE.
 //
 // Work items are mapped XCD-aware: workgroup i runs on XCD i % 8, and the items of one XCD are
-// contiguous in the work list, so the items of one bucket share that XCD's L2 for the block.
+// contiguous in the work list, so the items of one bucket share that XCD's L2 for the block (and,
+// with the g-major order, each XCD works through about one KV head's buckets).
 #include "msa_device.h"
 
 namespace msa {

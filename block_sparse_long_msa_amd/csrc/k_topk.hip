@@ -6,7 +6,8 @@
 // 32-bit keys and end with an in-order ballot pass that writes the chosen ids, which gives
 // ascending order and the lower-id tie rule for free.
 //   k_topk_reg (rows of up to 16384 blocks): the row sits in registers and the k-th largest key
-//     is found by bisection with ballot counts; the scores are read once.
+//     is found by bisection with ballot counts; the scores are read once.  The selection itself is
+//     row_topk (topk_select.h), shared with the fused decode select + attend kernel.
 //   k_topk (longer rows): radix select; it skips the bits every candidate shares, then takes
 //     8-bit digits from the top with an LDS histogram per pass, stopping as soon as the boundary
 //     digit's bucket is taken whole.
