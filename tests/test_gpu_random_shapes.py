@@ -21,19 +21,25 @@ def _ctx(rng, lo, hi):
     return L - L % 128 if rng.random() < 0.25 and L >= 128 else L   # some exact block multiples
 
 
-def _common(rng):
-    Hkv = int(rng.choice([1, 2, 4]))
+def _common(rng, kv_heads=(1, 2, 4)):
+    Hkv = int(rng.choice(kv_heads))
     G = int(rng.choice([1, 2, 4, 8, 16]))
+    while Hkv * G > 128:
+        G //= 2
     return dict(Hq=Hkv * G, Hkv=Hkv, D=int(rng.choice([64, 128])), Di=int(rng.choice([64, 128])),
                 k=int(rng.integers(1, 65)))
 
 
 def decode_case(seed):
+    """Up to 8 requests of up to 16 queries; KV heads up to 16 (Hkv*Di > 1024 takes the direct
+    scorer); planted hot blocks in some cases."""
     rng = np.random.default_rng(5000 + seed)
-    B = int(rng.integers(1, 7))
-    ctx = [_ctx(rng, 1, 6000) for _ in range(B)]
+    B = int(rng.integers(1, 9))
+    ctx = [_ctx(rng, 1, 8000) for _ in range(B)]
     nq = [int(rng.integers(1, min(16, L) + 1)) for L in ctx]
-    return mi.small_workload(ctx, nq, seed=5000 + seed, **_common(rng))
+    hot = int(rng.choice([0, 0, 4]))
+    return mi.small_workload(ctx, nq, seed=5000 + seed, hot_per_group=hot,
+                             **_common(rng, kv_heads=(1, 2, 3, 4, 8, 16)))
 
 
 def prefill_case(seed):
@@ -44,7 +50,7 @@ def prefill_case(seed):
     return mi.small_workload(ctx, nq, seed=6000 + seed, **_common(rng))
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(10))
 def test_random_decode_shapes(seed):
     wl = decode_case(seed)
     announce("random decode", f"seed {seed}: ctx {wl.ctx_lens} nq {wl.q_counts} Hkv {wl.Hkv} G {wl.G} "
