@@ -4,16 +4,20 @@
 // (the max is this library's reading of "each 128-token block is reduced to one score",
 // Chinese page of the MiniMax-M3 serving write-up, section "索引评分器成为解码关键路径").
 //
-// Two kernels, picked by queries per request:
-//  * k_score_decode: one workgroup per (request, block).  The 128-token key-index block is
-//    the MFMA M dimension and the request's (at most 16) queries are padded only into N
-//    -- the AB-swapped layout the pages describe for the decode scorer.  Each page of the
-//    key-index cache is read exactly once per request, straight from HBM into MFMA
-//    operand registers (every 16-lane group reads whole 64-byte segments of a token row).
+// Kernels, picked by queries per request:
+//  * decode (at most 16 queries per request): the 128-token key-index block is the MFMA M
+//    dimension and the request's queries are padded only into N -- the AB-swapped layout the
+//    pages describe for the decode scorer -- and each page of the key-index cache is read
+//    exactly once per request.
+//    - k_score_decode_lds (Hkv * Di <= 1024, the usual case): a workgroup streams consecutive
+//      blocks of one request through a double-buffered LDS stage with fully coalesced loads.
+//    - k_score_decode (larger rows): one workgroup per (request, block), loading straight from
+//      HBM into MFMA operand registers (every 16-lane group reads whole 64-byte segments).
 //  * k_score_prefill: one workgroup per (256 query rows, KV head).  A GEMM over the causal
 //    range, staging each key-index block in LDS once for 256 queries whose index vectors
 //    stay in registers, with the per-block max fused into the epilogue so that token-level
-//    scores never reach memory.
+//    scores never reach memory.  With TOPK > 0 the same kernel keeps each row's top-k on chip
+//    instead of writing scores (msa_index_topk).
 #include <type_traits>
 
 #include "msa_device.h"
