@@ -354,6 +354,28 @@ def test_paged_decode_attention_equals_block_table_attention():
     np.testing.assert_allclose(l2.reshape(lse.shape), lse, rtol=0, atol=1e-12)
 
 
+def test_decode_equals_last_prefill_token():
+    """One query at pos = L - 1 (decode: page table over strided views, one attention per row)
+    gives what the prefill of the whole context gives for its last token (KV-block-major lists,
+    per-block partials, LSE merge): the two routes share only the score and selection steps."""
+    x = _tiny([203], [203], Hq=4, Hkv=2, D=8, k=4, seed=19)
+    Nq, Hkv, G, D, BS = 203, x.wl.Hkv, x.wl.G, x.wl.D, x.wl.block
+    _, sel, cnt = _select(x)
+    po, pl = oracle.block_partials(x.q, x.kcache, x.vcache, x.block_table, x.ctx_len, x.q_req, x.q_pos,
+                                   sel, cnt, BS, x.scale)
+    o_pre, l_pre = oracle.lse_merge(po, pl)                       # [Nq, Hkv, G, D], [Nq, Hkv, G]
+    last = slice(Nq - 1, Nq)
+    assert int(x.q_pos[-1]) == int(x.ctx_len[0]) - 1
+    s_dec = oracle.index_scores(x.q_idx[last], x.kidx, x.block_table, x.ctx_len, x.q_req[last], x.q_pos[last], BS)
+    sel_d, cnt_d = oracle.topk_blocks(s_dec, x.q_pos[last], BS, x.wl.k)
+    pt, rl = oracle.sparse_page_table(sel_d, cnt_d, x.block_table, x.ctx_len, x.q_req[last], x.q_pos[last], Hkv, BS)
+    o_dec, l_dec = oracle.paged_decode_attention(x.q[last].reshape(Hkv, G, D), x.kcache, x.vcache, pt, rl, D,
+                                                 Hkv * D, BS, x.scale)
+    assert np.array_equal(sel_d[0], sel[-1]) and np.array_equal(cnt_d[0], cnt[-1])
+    np.testing.assert_allclose(o_dec, o_pre[-1], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l_dec, l_pre[-1], rtol=0, atol=1e-12)
+
+
 def test_kv_block_major_lists_invert_the_selection():
     x = _tiny([300], [50], k=3, seed=18)
     _, sel, cnt = _select(x)
