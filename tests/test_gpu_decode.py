@@ -41,6 +41,8 @@ CASES = {
     "topk_radix_long_rows": dict(ctx=[2100000], nq=[1], Hq=4, Hkv=1, D=64, Di=64, k=9),
     # the largest k and G: a row split into up to 64 page runs, merged over 64 parts
     "k64_g16_split": dict(ctx=[9000, 8300], nq=[1, 1], Hq=32, Hkv=2, D=128, Di=64, k=64),
+    # the most KV heads the library takes (64, one query head each) with the largest k
+    "hkv64_g1_k64": dict(ctx=[9000, 700], nq=[1, 2], Hq=64, Hkv=64, D=64, Di=64, k=64),
 }
 GPU_DRAWN = {"topk_16_waves", "topk_radix_long_rows"}   # inputs drawn on the GPU, copied to the host
 

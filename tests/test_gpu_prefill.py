@@ -24,6 +24,8 @@ CASES = {
     "g2_k_over_candidates": dict(ctx=[400, 129], nq=[250, 129], Hq=4, Hkv=2, D=64, Di=64, k=8),
     # the largest k and G the library takes: 64 slots per row, 64 parts x 16 heads in the merge
     "k64_g16": dict(ctx=[9000], nq=[300], Hq=32, Hkv=2, D=64, Di=64, k=64),
+    # the most KV heads the library takes (64, one query head each) with the largest k
+    "hkv64_g1_k64": dict(ctx=[9000], nq=[8], Hq=64, Hkv=64, D=128, Di=64, k=64),
     # many short requests in one chunk: work items from many buckets, rows of many requests
     "many_requests": dict(ctx=[300 + 37 * i for i in range(40)], nq=[1 + (i % 7) * 9 for i in range(40)], Hq=16,
                           Hkv=4, D=128, Di=64, k=3),
