@@ -249,7 +249,9 @@ def make_inputs(wl: Workload, device="cpu") -> Inputs:
     if wl.tie_frac > 0:
         for r in range(B):
             full = wl.ctx_lens[r] // BS
-            nt = max(1, int(round(wl.tie_frac * full)))
+            if full < 2:
+                continue  # a tie needs two full blocks
+            nt = min(max(1, int(round(wl.tie_frac * full))), full // 2)
             for g in range(Hkv):
                 pairs = []
                 picks = rng.choice(full, size=2 * nt, replace=False)
