@@ -293,6 +293,16 @@ constexpr int kPrefTQ = 256;  // query rows per workgroup (64 per wave)
 constexpr int kPrefSB = 16;   // blocks buffered per score flush
 constexpr int kFusedTopK = 16;  // largest k the fused scorer + top-k keeps per row
 
+// Slot swizzle of the staged key-index rows: logical 16-byte chunk c of token row `row` is stored at
+// chunk slot c ^ kidx_slot(row).  An MFMA operand read takes the same chunk of 16 consecutive rows;
+// with the swizzle those 16 reads cover all 64 LDS banks.  DI = 128 (256-byte rows, 16 slots): the
+// row's low four bits.  DI = 64 (128-byte rows, two rows per bank cycle): rows of equal parity get
+// distinct slots.
+template <int DI>
+__device__ __forceinline__ int kidx_slot(int row) {
+  return DI == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+
 // TOPK == 0: write the block scores.  TOPK > 0: fused top-k (k <= TOPK, block ids < 65536).  After
 // the cross-lane max every lane holds all four of its wave's row maxima, so lane (n, qd) adopts row
 // 16*qd + n of its wave and keeps that row's best k (score, block) pairs in its own registers.  Blocks
@@ -306,16 +316,22 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
     const bf16* __restrict__ kidx, int Hkv, float* __restrict__ scores, int k, int32_t* __restrict__ sel,
     int32_t* __restrict__ cnt) {
   constexpr int KW = DI / 32;
-  constexpr int KPAD = DI + 8;  // LDS row stride (elements): 16-lane ds_read_b128 groups hit 64 distinct banks
-  __shared__ __attribute__((aligned(16))) bf16 ks[kBlock * KPAD];
-  __shared__ float sbuf[TOPK == 0 ? kPrefTQ : 1][kPrefSB + 1];
-  __shared__ int wred[2][4];
+  constexpr int BLKE = kBlock * DI;  // elements of one staged key-index block
+  constexpr int CPR = DI / 8;        // 16-byte chunks per token row
+  constexpr int kLoadsPerWave = kBlock * CPR / 64 / 4;  // 64-chunk loads per wave per block
+  // Two buffers (the next block arrives while the current one is multiplied) of unpadded token rows
+  // in 16-byte chunks, swizzled by kidx_slot, plus the score buffer: 80 KiB at DI = 128, so two
+  // workgroups share a CU.  The score buffer's first words also carry the position reduction.
+  __shared__ __attribute__((aligned(16))) bf16 ks[2][BLKE];
+  __shared__ float sbuf[TOPK == 0 ? kPrefTQ : 1][TOPK == 0 ? kPrefSB : 8];
+  int* wred = reinterpret_cast<int*>(&sbuf[0][0]);
 
   const int g = blockIdx.x % Hkv;  // consecutive workgroups take consecutive KV heads
   // Row tiles go from the last to the first: a request's later rows have longer causal ranges, so
   // the longest tiles start first and the short ones fill the end of the launch.
   const int row0 = ((int)gridDim.x / Hkv - 1 - (int)blockIdx.x / Hkv) * kPrefTQ;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, qd = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, qd = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int last_row = min(row0 + kPrefTQ, Nq) - 1;
   const int r_first = request_of(cu_q, B, row0), r_last = request_of(cu_q, B, last_row);
 
@@ -343,10 +359,11 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
       pmax = max(pmax, __shfl_xor(pmax, m, kWave));
       pmin = min(pmin, __shfl_xor(pmin, m, kWave));
     }
-    if (lane == 0) { wred[0][w] = pmax; wred[1][w] = pmin; }
+    __syncthreads();  // the previous request's flush has read sbuf, which wred overlays
+    if (lane == 0) { wred[w] = pmax; wred[4 + w] = pmin; }
     __syncthreads();
-    pmax = max(max(wred[0][0], wred[0][1]), max(wred[0][2], wred[0][3]));
-    pmin = min(min(wred[1][0], wred[1][1]), min(wred[1][2], wred[1][3]));
+    pmax = max(max(wred[0], wred[1]), max(wred[2], wred[3]));
+    pmin = min(min(wred[4], wred[5]), min(wred[6], wred[7]));
     const int nb = pmax / kBlock + 1;  // blocks needed by at least one row
 
     // fused top-k state of the row this lane adopts (TOPK > 0)
@@ -390,29 +407,49 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
       }
     };
 
-    // key-index block b+1 is loaded into registers while block b is multiplied from LDS
-    u32x4 stage[DI / 16];
-    auto load_block = [&](int bb) {
+    // Block bb goes straight from HBM into LDS buffer buf (global_load_lds_dwordx4: each lane's 16
+    // bytes land at the LDS address in m0 plus 16 * lane).  Load i of wave w fills the 64 chunks of
+    // group 4i + w, i.e. 64 / CPR whole token rows: lane l loads, for row grp * 64 / CPR + l / CPR, the
+    // logical chunk that belongs in slot p = l % CPR, which is chunk p ^ kidx_slot(row).
+    //
+    // The loads are issued from inline assembly so that the compiler's wait-count pass does not see
+    // them: it cannot tell the two buffers apart and would wait for these loads before the first
+    // read of the buffer being multiplied.  The waits are explicit instead: a wave's loads of block
+    // b are complete at the s_waitcnt that precedes the barrier opening block b, and the next block's
+    // loads are issued only after that barrier, when no wave reads their buffer any more.  The LDS
+    // address goes through m0, which the assembly saves and restores; s_nop 0 gives the one wait
+    // state an LDS DMA needs after m0 is written, and one more before m0 is written back.
+    auto issue_block = [&](int bb, int buf) {
       const int page = block_table[(int64_t)r * max_blocks + bb];
       const bf16* kb = kidx + ((int64_t)page * kBlock * Hkv + g) * DI;
 #pragma unroll
-      for (int c = 0; c < DI / 16; ++c) {
-        const int idx = tid + 256 * c, tok = idx / (DI / 8), ch = idx % (DI / 8);
-        stage[c] = ld16(kb + (int64_t)tok * Hkv * DI + ch * 8);
+      for (int i = 0; i < kLoadsPerWave; ++i) {
+        const int grp = 4 * i + w;                         // wave-uniform group of 64 chunks
+        const int row = grp * (64 / CPR) + lane / CPR, p = lane % CPR;
+        const bf16* src = kb + (int64_t)row * Hkv * DI + 8 * (p ^ kidx_slot<DI>(row));
+        const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)(&ks[buf][grp * 64 * 8]);
+        uint32_t m0_saved;  // m0 is left as the compiler had it
+        asm volatile(
+            "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\t"
+            "s_nop 0\n\ts_mov_b32 m0, %0"
+            : "=&s"(m0_saved)
+            : "s"(dst), "v"(src)
+            : "memory");
       }
     };
-    load_block(0);
+    issue_block(0, 0);
     for (int b0 = 0; b0 < nb; b0 += kPrefSB) {
       const int b1 = min(b0 + kPrefSB, nb);
       for (int b = b0; b < b1; ++b) {
-        __syncthreads();  // previous block fully consumed
-#pragma unroll
-        for (int c = 0; c < DI / 16; ++c) {
-          const int idx = tid + 256 * c, tok = idx / (DI / 8), ch = idx % (DI / 8);
-          st16(&ks[tok * KPAD + ch * 8], stage[c]);
-        }
-        __syncthreads();
-        if (b + 1 < nb) load_block(b + 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of block b are in LDS
+        __syncthreads();  // every wave's are, and no wave reads the other buffer any more
+        if (b + 1 < nb) issue_block(b + 1, (b & 1) ^ 1);
+        const bf16* kbuf = ks[b & 1];
+        // operand of 16-token tile mt, k window kw for lane (n, qd): row 16mt + n, logical chunk 4kw + qd
+        auto frag = [&](int mt, int kw) {
+          const int row = 16 * mt + n;
+          return ld16(&kbuf[row * DI + (((4 * kw + qd) ^ kidx_slot<DI>(row)) << 3)]);
+        };
 
         // full blocks (every key valid for every row) take the unmasked body; the branch is uniform
         const bool full = (b * kBlock + kBlock - 1 <= pmin) && (b * kBlock + kBlock - 1 < L);
@@ -421,13 +458,13 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
           constexpr bool MASKED = decltype(masked)::value;
           u32x4 a_cur[KW];
 #pragma unroll
-          for (int kw = 0; kw < KW; ++kw) a_cur[kw] = ld16(&ks[n * KPAD + 32 * kw + 8 * qd]);
+          for (int kw = 0; kw < KW; ++kw) a_cur[kw] = frag(0, kw);
 #pragma unroll
           for (int mt = 0; mt < 8; ++mt) {
             u32x4 a_nxt[KW];  // next 16-token tile's operands, read while this one multiplies
             if (mt < 7) {
 #pragma unroll
-              for (int kw = 0; kw < KW; ++kw) a_nxt[kw] = ld16(&ks[(16 * (mt + 1) + n) * KPAD + 32 * kw + 8 * qd]);
+              for (int kw = 0; kw < KW; ++kw) a_nxt[kw] = frag(mt + 1, kw);
             }
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
