@@ -59,7 +59,7 @@ def test_random_decode_shapes(seed):
     check_decode(dev, cpu)
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(10))
 def test_random_prefill_shapes(seed):
     wl = prefill_case(seed)
     announce("random prefill", f"seed {seed}: ctx {wl.ctx_lens} nq {wl.q_counts} Hkv {wl.Hkv} G {wl.G} "
