@@ -303,12 +303,44 @@ __device__ __forceinline__ int kidx_slot(int row) {
   return DI == 128 ? (row & 15) : ((row >> 1) & 7);
 }
 
-// TOPK == 0: write the block scores.  TOPK > 0: fused top-k (k <= TOPK, block ids < 65536).  After
-// the cross-lane max every lane holds all four of its wave's row maxima, so lane (n, qd) adopts row
-// 16*qd + n of its wave and keeps that row's best k (score, block) pairs in its own registers.  Blocks
-// arrive in ascending id, so a new block enters only if it beats the current worst entry strictly
-// (equal scores keep the lower id), and the worst entry -- lowest score, highest id among equals --
-// is the one evicted.  The result equals msa_topk_blocks applied to the written scores.
+// Bitonic networks over N (a power of two) 64-bit keys held in registers, larger keys first.
+__device__ __forceinline__ void cas_desc(uint64_t& a, uint64_t& b) {
+  const bool sw = a < b;
+  const uint64_t hi = sw ? b : a, lo = sw ? a : b;
+  a = hi;
+  b = lo;
+}
+template <int N>
+__device__ __forceinline__ void bitonic_merge_desc(uint64_t (&v)[N]) {  // v bitonic -> sorted
+#pragma unroll
+  for (int stride = N / 2; stride > 0; stride >>= 1)
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if ((i & stride) == 0) cas_desc(v[i], v[i + stride]);
+}
+template <int N>
+__device__ __forceinline__ void bitonic_sort_desc(uint64_t (&v)[N]) {
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1)
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if ((i & stride) == 0) {
+          if ((i & size) == 0) cas_desc(v[i], v[i + stride]);  // this run descending
+          else cas_desc(v[i + stride], v[i]);                  // this run ascending
+        }
+}
+
+// TOPK == 0: write the block scores.  TOPK > 0: fused top-k (k <= TOPK = 16).  Thread t of the
+// workgroup adopts local row t and keeps that row's best 16 candidates in registers, as 64-bit keys
+// (order-preserving score bits above the complement of the block id, so a larger key is a higher
+// score or, at equal scores, a lower block id -- the library's tie rule), sorted best first.  The
+// block maxima are buffered in LDS as for the score output; every 16 blocks each thread sorts its
+// row's 16 new keys with a bitonic network, keeps the larger of kept[i] and new[15 - i] (the best 16
+// of both lists, a bitonic sequence) and re-sorts them with a bitonic merge.  The work is the same
+// for every row, so no lane waits on another's insertions.  The result equals msa_topk_blocks applied
+// to the written scores.
 template <int DI, int TOPK>
 __global__ __launch_bounds__(256, 2) void k_score_prefill(
     int B, int Nq, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ ctx_len,
@@ -323,7 +355,7 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
   // in 16-byte chunks, swizzled by kidx_slot, plus the score buffer: 80 KiB at DI = 128, so two
   // workgroups share a CU.  The score buffer's first words also carry the position reduction.
   __shared__ __attribute__((aligned(16))) bf16 ks[2][BLKE];
-  __shared__ float sbuf[TOPK == 0 ? kPrefTQ : 1][TOPK == 0 ? kPrefSB : 8];
+  __shared__ float sbuf[kPrefTQ][kPrefSB];
   int* wred = reinterpret_cast<int*>(&sbuf[0][0]);
 
   const int g = blockIdx.x % Hkv;  // consecutive workgroups take consecutive KV heads
@@ -366,46 +398,13 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
     pmin = min(min(wred[4], wred[5]), min(wred[6], wred[7]));
     const int nb = pmax / kBlock + 1;  // blocks needed by at least one row
 
-    // fused top-k state of the row this lane adopts (TOPK > 0)
-    const int lr = 64 * w + 16 * qd + n;  // local row
-    int my_last = -1;                     // last candidate block of the adopted row
+    // fused top-k state (TOPK > 0) of local row tid: its last candidate block and its best keys
+    const int arow = row0 + tid;
+    const int my_last = (TOPK > 0 && arow >= qa && arow < qb) ? q_pos[arow] / kBlock : -1;
+    constexpr int TK = TOPK > 0 ? TOPK : 1;
+    uint64_t kept[TK];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
-      if (nt == qd && pos[nt] >= 0) my_last = pos[nt] / kBlock;
-    int n_in = 0, worst_slot = 0, worst_id = 0;
-    float worst = neg_inf();
-    // the kept entries live in registers: scores, and block ids packed two per 32-bit word
-    constexpr int TK = TOPK > 0 ? TOPK : 2;
-    float top_s[TK];
-    uint32_t top_i[TK / 2];
-#pragma unroll
-    for (int j = 0; j < TK; ++j) top_s[j] = __builtin_inff();
-#pragma unroll
-    for (int j = 0; j < TK / 2; ++j) top_i[j] = 0u;
-    auto id_of = [&](int j) -> int { return (int)((top_i[j >> 1] >> (16 * (j & 1))) & 0xffffu); };
-    auto put = [&](int slot, float v, int id) {
-#pragma unroll
-      for (int j = 0; j < TK; ++j) {
-        top_s[j] = j == slot ? v : top_s[j];
-        if (j == slot) {
-          const int sh = 16 * (j & 1);
-          top_i[j >> 1] = (top_i[j >> 1] & ~(0xffffu << sh)) | ((uint32_t)id << sh);
-        }
-      }
-    };
-    auto rescan = [&]() {  // worst entry: lowest score, highest block id among equal scores
-      worst = __builtin_inff();
-      worst_id = -1;
-#pragma unroll
-      for (int j = 0; j < TK; ++j) {
-        const float sj = top_s[j];
-        const int ij = id_of(j);
-        const bool worse = j < k && (sj < worst || (sj == worst && ij > worst_id));
-        worst = worse ? sj : worst;
-        worst_id = worse ? ij : worst_id;
-        worst_slot = worse ? j : worst_slot;
-      }
-    };
+    for (int j = 0; j < TK; ++j) kept[j] = 0;  // 0 ranks below every candidate key
 
     // Block bb goes straight from HBM into LDS buffer buf (global_load_lds_dwordx4: each lane's 16
     // bytes land at the LDS address in m0 plus 16 * lane).  Load i of wave w fills the 64 chunks of
@@ -489,37 +488,32 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
         };
         if (full) block_body(std::false_type{});
         else block_body(std::true_type{});
-        if constexpr (TOPK == 0) {
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            const float v = max_over_quads(mx[nt]);
-            if (qd == 0) sbuf[64 * w + 16 * nt + n][b - b0] = v;
-          }
-        } else {
-          float mine = neg_inf();
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            const float v = max_over_quads(mx[nt]);
-            mine = nt == qd ? v : mine;
-          }
-          if (b <= my_last) {
-            if (n_in < k) {
-              put(n_in, mine, b);
-              if (++n_in == k) rescan();
-            } else if (mine > worst) {
-              put(worst_slot, mine, b);
-              rescan();
-            }
-          }
+        for (int nt = 0; nt < 4; ++nt) {
+          const float v = max_over_quads(mx[nt]);
+          if (qd == 0) sbuf[64 * w + 16 * nt + n][b - b0] = v;
         }
       }
+      __syncthreads();
       if constexpr (TOPK == 0) {
-        __syncthreads();
         // flush: 16 consecutive threads write 16 consecutive blocks of one row
         for (int it = 0; it < kPrefTQ / 16; ++it) {
           const int lrow = it * 16 + (tid >> 4), bb = tid & 15, row = row0 + lrow, b = b0 + bb;
           if (row >= qa && row < qb && b < b1) scores[((int64_t)row * Hkv + g) * max_blocks + b] = sbuf[lrow][bb];
         }
+      } else {
+        static_assert(TOPK == kPrefSB, "one bitonic merge per flush of 16 blocks");
+        uint64_t nk[TK];
+#pragma unroll
+        for (int j = 0; j < TK; ++j) {
+          const int b = b0 + j;
+          const bool cand = b < b1 && b <= my_last;
+          nk[j] = cand ? ((uint64_t)order_key(sbuf[tid][j]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)b) : 0ull;
+        }
+        bitonic_sort_desc<TK>(nk);
+#pragma unroll
+        for (int j = 0; j < TK; ++j) kept[j] = kept[j] > nk[TK - 1 - j] ? kept[j] : nk[TK - 1 - j];
+        bitonic_merge_desc<TK>(kept);
       }
     }
     if constexpr (TOPK == 0) {
@@ -529,27 +523,25 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
         const int row = qa + e / tail, b = nb + e % tail;
         scores[((int64_t)row * Hkv + g) * max_blocks + b] = neg_inf();
       }
-    } else {
-      const int row = row0 + lr;
-      if (row >= qa && row < qb) {
-        int ids[TOPK];
+    } else if (arow >= qa && arow < qb) {
+      // the first min(k, candidates) keys, as block ids in ascending order
+      const int c = min(k, my_last + 1);
+      int ids[TK];
 #pragma unroll
-        for (int j = 0; j < TOPK; ++j) ids[j] = j < n_in ? id_of(j) : 0x7fffffff;
+      for (int j = 0; j < TK; ++j) ids[j] = j < c ? (int)(0xffffffffu - (uint32_t)kept[j]) : 0x7fffffff;
 #pragma unroll
-        for (int a = 0; a < TOPK; ++a)  // ascending block ids (odd-even transposition sort)
+      for (int a = 0; a < TK; ++a)  // ascending block ids (odd-even transposition sort)
 #pragma unroll
-          for (int j = a & 1; j + 1 < TOPK; j += 2) {
-            const int lo = min(ids[j], ids[j + 1]), hi = max(ids[j], ids[j + 1]);
-            ids[j] = lo;
-            ids[j + 1] = hi;
-          }
-        int32_t* out = sel + ((int64_t)row * Hkv + g) * k;
+        for (int j = a & 1; j + 1 < TK; j += 2) {
+          const int lo = min(ids[j], ids[j + 1]), hi = max(ids[j], ids[j + 1]);
+          ids[j] = lo;
+          ids[j + 1] = hi;
+        }
+      int32_t* out = sel + ((int64_t)arow * Hkv + g) * k;
 #pragma unroll
-        for (int j = 0; j < TOPK; ++j)
-          if (j < k) out[j] = j < n_in ? ids[j] : -1;
-        for (int j = TOPK; j < k; ++j) out[j] = -1;
-        cnt[(int64_t)row * Hkv + g] = n_in;
-      }
+      for (int j = 0; j < TK; ++j)
+        if (j < k) out[j] = j < c ? ids[j] : -1;
+      cnt[(int64_t)arow * Hkv + g] = c;
     }
     __syncthreads();
   }

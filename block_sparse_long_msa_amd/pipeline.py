@@ -2,7 +2,8 @@
 
 MSADecode: index scores -> top-k + sparse page table + decode attention (split over pages,
            merged in the library), by default in one call after the scores.
-MSAPrefill: index scores -> top-k -> KV-block-major attention (partials) -> LSE merge.
+MSAPrefill: index scores + top-k (one fused call by default) -> KV-block-major attention (partials)
+           -> LSE merge.
 MSAPrefillQueryMajor: the query-major baseline the KV-block-major mapping is measured against:
            index scores -> top-k + page table -> every (query token, KV head) row attends to its own
            k blocks with the paged decode kernel (no partials, no merge, K/V re-read per row).
@@ -80,12 +81,13 @@ class MSADecode:
 
 
 class MSAPrefill:
-    """``fused=True`` scores and selects in one call (msa_index_topk): block scores never reach memory
-    when the shape allows it, and ``scores`` is then not kept.  The two-call route is the default: on
-    the long-prefill workload it is still slightly faster."""
+    """``fused=True`` (the default) scores and selects in one call (msa_index_topk): for k <= 16 the
+    block scores never reach memory and ``scores`` is not kept; on the long-prefill workload this is
+    faster than the two calls.  ``fused=False`` runs msa_index_score then msa_topk_blocks and keeps the
+    scores."""
 
     def __init__(self, batch: Batch, Hkv: int, G: int, D: int, k: int, num_pages: int, device="cuda",
-                 fused: bool = False):
+                 fused: bool = True):
         Nq, mb = batch.num_queries, batch.max_blocks
         self.batch, self.Hkv, self.G, self.D, self.k, self.num_pages = batch, Hkv, G, D, k, num_pages
         self.fused = fused

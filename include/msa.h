@@ -103,9 +103,9 @@ msa_status msa_topk_blocks(const msa_batch* batch, int32_t num_kv_heads, const f
  * per-block scoring and reduction) as the open opportunity (Chinese page, section "遗留问题";
  * Japanese page, "今後の取り組み").  The result is identical to msa_index_score followed by
  * msa_topk_blocks -- same fp32 block scores, same tie rule -- but for prefill shapes
- * (batch->max_q_per_request > 16) with k <= 16 the block scores never reach memory: the scoring
- * kernel keeps every query row's running top-k on chip.  Other shapes run the two kernels through
- * the workspace.
+ * (batch->max_q_per_request > 16) with k <= 16 and max_blocks <= 65536 the block scores never reach
+ * memory: the scoring kernel keeps every query row's running top-16 on chip.  Other shapes run the
+ * two kernels through the workspace.
  *   sel, cnt   as msa_topk_blocks
  *   workspace  device, >= msa_index_topk_workspace_size(...) bytes (may be 0 / NULL) */
 msa_status msa_index_topk(const msa_batch* batch, const void* q_idx, msa_cache k_idx, int32_t k, int32_t* sel,

@@ -57,13 +57,15 @@ def test_decode_step_replays_from_a_graph(mode):
     _check_replays(run, [run.scores, run.sel, run.cnt, run.page_table, run.row_len, run.out, run.lse], dev)
 
 
-def test_prefill_step_replays_from_a_graph():
-    announce("graph prefill")
+@pytest.mark.parametrize("fused", [True, False])
+def test_prefill_step_replays_from_a_graph(fused):
+    announce("graph prefill", "fused" if fused else "two calls")
     msa = lib()
     from block_sparse_long_msa_amd.pipeline import MSAPrefill
     wl = mi.small_workload([900, 2000], [300, 500], Hq=16, Hkv=2, D=128, Di=64, k=6, seed=42)
     dev, _ = setup(wl)
     b = msa.Batch(dev.block_table, dev.ctx_len, dev.cu_q, dev.q_pos, max(wl.q_counts))
-    run = MSAPrefill(b, wl.Hkv, wl.G, wl.D, wl.k, dev.kcache.shape[0])
+    run = MSAPrefill(b, wl.Hkv, wl.G, wl.D, wl.k, dev.kcache.shape[0], fused=fused)
     # part_o slots of absent parts are never written (their lse is -inf), so they are not compared
-    _check_replays(run, [run.scores, run.sel, run.cnt, run.part_lse, run.out, run.lse], dev)
+    outs = [run.sel, run.cnt, run.part_lse, run.out, run.lse] + ([] if fused else [run.scores])
+    _check_replays(run, outs, dev)
