@@ -305,7 +305,8 @@ def main():
     else:
         sel_tok = selected_tokens(dev, run.sel, run.cnt)
         score_flops = 2.0 * cand * wl.Hkv * wl.Di
-        roof = {"kernel": "k_score_prefill" + ("" if args.two_call_topk else " with fused top-k"), "bound": "mfma",
+        fused_prefill = not (args.two_call_topk or query_major)
+        roof = {"kernel": "k_score_prefill" + (" with fused top-k" if fused_prefill else ""), "bound": "mfma",
                 "achieved": score_flops / (score_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "traffic": None, "algorithmic_flops": score_flops, "avg_ms": score_ms}
         attn_flops = 4.0 * sel_tok * wl.G * wl.D               # QK^T and PV over the selected tokens
@@ -336,7 +337,7 @@ def main():
                    "query_tokens": wl.Nq, "ctx_len": wl.ctx_lens[0] if len(set(wl.ctx_lens)) == 1 else "ragged",
                    "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "Di": wl.Di, "top_k": wl.k, "block": wl.block,
                    "l2_flush_between_steps": flush is not None,
-                   "fused_index_topk": bool(not args.two_call_topk and not decode),
+                   "fused_index_topk": bool(not (args.two_call_topk or decode or args.prefill_mode == "query-major")),
                    "prefill_mode": None if decode else args.prefill_mode,
                    "kv_on_host": bool(kv_on_host),
                    "decode_select": args.decode_select if decode else None},
