@@ -19,6 +19,8 @@ CASES = {
     "many_requests_straddling_tiles": dict(ctx=[300, 200, 900, 129, 513], nq=[170, 100, 260, 129, 90], Hq=8, Hkv=2,
                                            D=64, Di=128, k=3),
     "k_over_candidates": dict(ctx=[400, 129], nq=[250, 129], Hq=4, Hkv=2, D=64, Di=64, k=12),
+    # exact score ties (bitwise copies of whole blocks) decided by the lower block id inside the fused kernel
+    "tied_blocks_k16": dict(ctx=[6000, 2600], nq=[300, 120], Hq=8, Hkv=2, D=64, Di=64, k=16, tie_frac=0.2),
     "k20_two_kernel_route": dict(ctx=[5000], nq=[300], Hq=8, Hkv=2, D=64, Di=64, k=20),
     "decode_two_kernel_route": dict(ctx=[5000, 2049, 777], nq=[1, 3, 1], Hq=16, Hkv=2, D=128, Di=128, k=8),
 }
