@@ -103,9 +103,11 @@ __global__ __launch_bounds__(256) void k_remap_count(int64_t E, int B, int Hkv, 
   }
 }
 
-// Exclusive scans of the bucket sizes and of their work-item counts (one workgroup).
+// Exclusive scans of the bucket sizes and of their work-item counts (one workgroup), and the work
+// list: bucket i's items (i, 0 .. n_i - 1) at item_off[i].
 __global__ __launch_bounds__(1024) void k_remap_scan(int64_t NB, const int32_t* __restrict__ counts,
-                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ item_off) {
+                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ item_off,
+                                                     int2* __restrict__ items) {
   __shared__ int32_t s_a[1024], s_b[1024];
   __shared__ int32_t carry[2];
   const int tid = threadIdx.x;
@@ -128,8 +130,10 @@ __global__ __launch_bounds__(1024) void k_remap_scan(int64_t NB, const int32_t* 
     }
     const int32_t ca = carry[0], cb = carry[1];
     if (i < NB) {
+      const int32_t io = cb + s_b[tid] - b;
       offsets[i] = ca + s_a[tid] - a;
-      item_off[i] = cb + s_b[tid] - b;
+      item_off[i] = io;
+      for (int j = 0; j < b; ++j) items[io + j] = make_int2((int)i, j);
     }
     __syncthreads();
     if (tid == 1023) { carry[0] = ca + s_a[1023]; carry[1] = cb + s_b[1023]; }
@@ -281,15 +285,6 @@ __global__ __launch_bounds__(256) void k_remap_fill_lds(RemapArgs a, int run, in
     for (int u = 0; u < kRemapU; ++u)
       if (bucket[u] >= 0) entries[atomicAdd(&hist[bucket[u]], 1)] = code[u];
   }
-}
-
-__global__ __launch_bounds__(256) void k_remap_items(int64_t NB, const int32_t* __restrict__ counts,
-                                                     const int32_t* __restrict__ item_off, int2* __restrict__ items) {
-  const int64_t bucket = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (bucket >= NB) return;
-  const int n = (counts[bucket] + kChunk - 1) / kChunk;
-  const int base = item_off[bucket];
-  for (int c = 0; c < n; ++c) items[base + c] = make_int2((int)bucket, c);
 }
 
 // V^T in LDS: row d holds the block's 128 tokens in 4-token (8-byte) chunks; chunk c of row d is
@@ -559,9 +554,10 @@ hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blo
   const int64_t NB = (int64_t)Hkv * B * max_blocks;
   const int64_t E = (int64_t)Nq * Hkv * k;
   PrefillWs ws = carve(workspace, NB, E);
-  const int fill_blocks = (int)((NB + 255) / 256 < 4096 ? (NB + 255) / 256 : 4096);
-  hipLaunchKernelGGL(k_fill_i32, dim3(fill_blocks), dim3(256), 0, stream, ws.counts, NB, 0);
-  hipLaunchKernelGGL(k_fill_i32, dim3(fill_blocks), dim3(256), 0, stream, ws.cursor, NB, 0);
+  // counts and cursor are adjacent in the workspace: one fill clears both
+  const int64_t n_clear = (int64_t)(ws.offsets - ws.counts);
+  const int fill_blocks = (int)((n_clear + 255) / 256 < 4096 ? (n_clear + 255) / 256 : 4096);
+  hipLaunchKernelGGL(k_fill_i32, dim3(fill_blocks), dim3(256), 0, stream, ws.counts, n_clear, 0);
   const unsigned eb = (unsigned)((E + 255) / 256);
   const bool lds_remap = NB <= kLdsBuckets;
   const int run = remap_run(E);
@@ -572,15 +568,14 @@ hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blo
   else
     hipLaunchKernelGGL(k_remap_count, dim3(eb), dim3(256), 0, stream, E, B, Hkv, k, G, max_blocks, cu_q, sel, cnt,
                        ws.counts, part_lse);
-  hipLaunchKernelGGL(k_remap_scan, dim3(1), dim3(1024), 0, stream, NB, ws.counts, ws.offsets, ws.item_off);
+  hipLaunchKernelGGL(k_remap_scan, dim3(1), dim3(1024), 0, stream, NB, ws.counts, ws.offsets, ws.item_off,
+                     ws.items);
   if (lds_remap)
     hipLaunchKernelGGL(k_remap_fill_lds, dim3(rb), dim3(256), 0, stream, ra, run, (int)NB, ws.offsets, ws.cursor,
                        ws.entries);
   else
     hipLaunchKernelGGL(k_remap_fill, dim3(eb), dim3(256), 0, stream, E, B, Hkv, k, max_blocks, cu_q, sel, cnt,
                        ws.offsets, ws.cursor, ws.entries);
-  hipLaunchKernelGGL(k_remap_items, dim3((unsigned)((NB + 255) / 256)), dim3(256), 0, stream, NB, ws.counts,
-                     ws.item_off, ws.items);
   // upper bound on the work items, rounded up to whole XCD rounds
   const int64_t mi = max_items(E, NB);
   const unsigned grid = (unsigned)(((mi + kXcds - 1) / kXcds) * kXcds);
