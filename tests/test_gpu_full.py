@@ -86,14 +86,16 @@ def test_agentic_decode_full():
     _check_requests_decode(dev, run, m, [0, 5], s, sel, cnt, out, exact_hot=True)
 
 
-def test_million_decode_full():
-    wl = mi.million_decode(batch=1)
+@pytest.mark.parametrize("batch", [1, 4])
+def test_million_decode_full(batch):
+    wl = mi.million_decode(batch=batch)
     announce("full", wl.name)
     dev = mi.make_inputs(wl, "cuda")
     run = _decode_run(dev)
     m = _host_meta(dev)
     s, sel, cnt, out = _check_all_rows_decode(dev, run, m)
-    _check_requests_decode(dev, run, m, [0], s, sel, cnt, out)     # all 8192 blocks of every KV head
+    # all 8192 blocks of every KV head of the last request (its rows sit past the others' pages)
+    _check_requests_decode(dev, run, m, [batch - 1], s, sel, cnt, out)
 
 
 def test_spec_decode_full():
