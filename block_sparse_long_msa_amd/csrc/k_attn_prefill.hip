@@ -8,8 +8,8 @@
 //
 // Remap (a counting sort):
 //   bucket = (KV head g, request r, logical block b), ordered g-major.  count -> exclusive scan
-//   -> scatter (t, j) into the bucket lists, plus a work list of (bucket, chunk of kChunk query
-//   tokens).  Order within a bucket is not fixed, but every (t, g, j) result is computed from its
+//   -> scatter (t, j) into the bucket lists, plus a work list of (bucket, chunk of up to 256 query
+//   tokens; smaller chunks when a launch would otherwise have too few items to fill the chip).  Order within a bucket is not fixed, but every (t, g, j) result is computed from its
 //   own query row only, so outputs are exact and reproducible whatever the order.
 //
 // k_attn_kvbm: one workgroup per work item.  It stages block b of KV head g in LDS once -- K
@@ -24,6 +24,8 @@
 // Work items are mapped XCD-aware: workgroup i runs on XCD i % 8, and the items of one XCD are
 // contiguous in the work list, so the items of one bucket share that XCD's L2 for the block (and,
 // with the g-major order, each XCD works through about one KV head's buckets).
+#include <algorithm>
+
 #include "msa_device.h"
 
 namespace msa {
@@ -37,7 +39,9 @@ namespace msa {
 #ifndef MSA_KVBM_OCC
 #define MSA_KVBM_OCC 2
 #endif
-constexpr int kChunk = 256;               // query tokens per work item
+constexpr int kChunk = 256;               // most query tokens per work item (LDS lists)
+constexpr int kMinChunk = 32;             // fewest query tokens per work item
+constexpr int kTargetItems = 1024;        // work items a launch aims for (about two per workgroup slot)
 constexpr int kNT = MSA_KVBM_NT;          // 16-row MFMA N tiles per wave per pass
 constexpr int kWaves = MSA_KVBM_WAVES;    // waves per workgroup, sharing one staged block
 constexpr int kThreads = 64 * kWaves;
@@ -56,14 +60,27 @@ struct PrefillWs {
 
 static size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
 
-static int64_t max_items(int64_t total_entries, int64_t NB) {
-  return total_entries / kChunk + (total_entries < NB ? total_entries : NB) + 1;
+// Upper bound on the work items: bucket i with c_i entries makes ceil(c_i / chunk) of them.
+static int64_t max_items(int64_t total_entries, int64_t NB, int chunk) {
+  return total_entries / chunk + (total_entries < NB ? total_entries : NB) + 1;
+}
+
+// Query tokens per work item: kChunk when that already makes enough items to fill the chip, else
+// halved until it does, but not below one pass of the workgroup's waves (kWaves * 16 * kNT rows,
+// i.e. that many / G tokens) or kMinChunk.  A row's partial does not depend on which item holds it,
+// so the choice changes the work split only.
+static int item_chunk(int64_t total_entries, int G) {
+  const int pass = std::max(kMinChunk, kWaves * 16 * kNT / G);
+  int c = kChunk;
+  while (c > pass && total_entries / c < kTargetItems) c >>= 1;
+  return c;
 }
 
 size_t prefill_workspace_bytes(int32_t Nq, int32_t Hkv, int32_t k, int32_t B, int32_t max_blocks) {
   const int64_t NB = (int64_t)Hkv * B * max_blocks;
   const int64_t E = (int64_t)Nq * Hkv * k;
-  return a256(NB * 4) * 2 + a256((NB + 1) * 4) * 2 + a256(E * 4) + a256(max_items(E, NB) * 8);
+  // the work list is sized for the smallest chunk, so it holds the list of any chunk item_chunk picks
+  return a256(NB * 4) * 2 + a256((NB + 1) * 4) * 2 + a256(E * 4) + a256(max_items(E, NB, kMinChunk) * 8);
 }
 
 static PrefillWs carve(void* ws, int64_t NB, int64_t E) {
@@ -104,8 +121,9 @@ __global__ __launch_bounds__(256) void k_remap_count(int64_t E, int B, int Hkv, 
 }
 
 // Exclusive scans of the bucket sizes and of their work-item counts (one workgroup), and the work
-// list: bucket i's items (i, 0 .. n_i - 1) at item_off[i].
-__global__ __launch_bounds__(1024) void k_remap_scan(int64_t NB, const int32_t* __restrict__ counts,
+// list: bucket i's items (i, 0 .. n_i - 1) at item_off[i], item j holding its entries
+// j*chunk .. j*chunk + chunk - 1.
+__global__ __launch_bounds__(1024) void k_remap_scan(int64_t NB, int chunk, const int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ item_off,
                                                      int2* __restrict__ items) {
   __shared__ int32_t s_a[1024], s_b[1024];
@@ -116,7 +134,7 @@ __global__ __launch_bounds__(1024) void k_remap_scan(int64_t NB, const int32_t* 
   for (int64_t base = 0; base < NB; base += 1024) {
     const int64_t i = base + tid;
     const int32_t c = i < NB ? counts[i] : 0;
-    int32_t a = c, b = (c + kChunk - 1) / kChunk;
+    int32_t a = c, b = (c + chunk - 1) / chunk;
     s_a[tid] = a;
     s_b[tid] = b;
     __syncthreads();
@@ -302,7 +320,7 @@ __global__ __launch_bounds__(kThreads, MSA_KVBM_OCC) void k_attn_kvbm(
     const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q,
     const bf16* __restrict__ kcache, const bf16* __restrict__ vcache, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ item_off, const int2* __restrict__ items, const int32_t* __restrict__ entries,
-    int64_t NB, float scale_log2, bf16* __restrict__ part_o, float* __restrict__ part_lse) {
+    int64_t NB, int chunk, float scale_log2, bf16* __restrict__ part_o, float* __restrict__ part_lse) {
   constexpr int KW = D / 32;        // 32-wide k windows over the head dimension
   constexpr int KS = kBlock / 32;   // 32-token k steps of the PV contraction
   constexpr int PAD = 8;            // LDS row padding (elements)
@@ -323,8 +341,8 @@ __global__ __launch_bounds__(kThreads, MSA_KVBM_OCC) void k_attn_kvbm(
   const int g = (int)(bucket / ((int64_t)B * max_blocks));
   const int rb = (int)(bucket % ((int64_t)B * max_blocks));
   const int r = rb / max_blocks, b = rb % max_blocks;
-  const int e_begin = offsets[bucket] + it.y * kChunk;
-  const int e_end = min(e_begin + kChunk, offsets[bucket + 1]);
+  const int e_begin = offsets[bucket] + it.y * chunk;
+  const int e_end = min(e_begin + chunk, offsets[bucket + 1]);  // chunk <= kChunk: fits s_tj
   const int L = ctx_len[r];
   const int page = block_table[(int64_t)r * max_blocks + b];
   const int in_block = min(kBlock, L - b * kBlock);  // tokens of the block that exist
@@ -568,7 +586,8 @@ hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blo
   else
     hipLaunchKernelGGL(k_remap_count, dim3(eb), dim3(256), 0, stream, E, B, Hkv, k, G, max_blocks, cu_q, sel, cnt,
                        ws.counts, part_lse);
-  hipLaunchKernelGGL(k_remap_scan, dim3(1), dim3(1024), 0, stream, NB, ws.counts, ws.offsets, ws.item_off,
+  const int chunk = item_chunk(E, G);
+  hipLaunchKernelGGL(k_remap_scan, dim3(1), dim3(1024), 0, stream, NB, chunk, ws.counts, ws.offsets, ws.item_off,
                      ws.items);
   if (lds_remap)
     hipLaunchKernelGGL(k_remap_fill_lds, dim3(rb), dim3(256), 0, stream, ra, run, (int)NB, ws.offsets, ws.cursor,
@@ -577,7 +596,7 @@ hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blo
     hipLaunchKernelGGL(k_remap_fill, dim3(eb), dim3(256), 0, stream, E, B, Hkv, k, max_blocks, cu_q, sel, cnt,
                        ws.offsets, ws.cursor, ws.entries);
   // upper bound on the work items, rounded up to whole XCD rounds
-  const int64_t mi = max_items(E, NB);
+  const int64_t mi = max_items(E, NB, chunk);
   const unsigned grid = (unsigned)(((mi + kXcds - 1) / kXcds) * kXcds);
   const float sl2 = sm_scale * kLog2eP;
   const bf16* qq = static_cast<const bf16*>(q);
@@ -586,11 +605,11 @@ hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blo
   bf16* po = static_cast<bf16*>(part_o);
   if (D == 128)
     hipLaunchKernelGGL(k_attn_kvbm<128>, dim3(grid), dim3(kThreads), 0, stream, B, Hkv, G, k, max_blocks, block_table,
-                       ctx_len, q_pos, qq, kc, vc, ws.offsets, ws.item_off, ws.items, ws.entries, NB, sl2, po,
+                       ctx_len, q_pos, qq, kc, vc, ws.offsets, ws.item_off, ws.items, ws.entries, NB, chunk, sl2, po,
                        part_lse);
   else
     hipLaunchKernelGGL(k_attn_kvbm<64>, dim3(grid), dim3(kThreads), 0, stream, B, Hkv, G, k, max_blocks, block_table,
-                       ctx_len, q_pos, qq, kc, vc, ws.offsets, ws.item_off, ws.items, ws.entries, NB, sl2, po,
+                       ctx_len, q_pos, qq, kc, vc, ws.offsets, ws.item_off, ws.items, ws.entries, NB, chunk, sl2, po,
                        part_lse);
   return hipGetLastError();
 }
