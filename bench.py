@@ -44,8 +44,8 @@ def parse():
     p.add_argument("--cpu-budget-s", type=float, default=12.0, help="oracle time budget for cpu_baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--two-call-topk", action="store_true",
-                   help="prefill: score and select with msa_index_score then msa_topk_blocks instead of the "
-                        "fused msa_index_topk (the default)")
+                   help="prefill: always score and select with msa_index_score then msa_topk_blocks (by "
+                        "default the fused msa_index_topk runs whenever its launch fills the chip)")
     p.add_argument("--prefill-mode", default="kvbm", choices=["kvbm", "query-major"],
                    help="prefill attention: KV-block-major with LSE merge (the method), or the query-major "
                         "baseline it is measured against (each row reads its own blocks)")
@@ -228,7 +228,7 @@ def main():
     elif query_major:
         run = MSAPrefillQueryMajor(b, wl.Hkv, wl.G, wl.D, wl.k, P)
     else:
-        run = MSAPrefill(b, wl.Hkv, wl.G, wl.D, wl.k, P, fused=not args.two_call_topk)
+        run = MSAPrefill(b, wl.Hkv, wl.G, wl.D, wl.k, P, fused=False if args.two_call_topk else None)
     flush = None
     if not args.no_flush:
         flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -309,7 +309,7 @@ def main():
     else:
         sel_tok = selected_tokens(dev, run.sel, run.cnt)
         score_flops = 2.0 * cand * wl.Hkv * wl.Di
-        fused_prefill = not (args.two_call_topk or query_major)
+        fused_prefill = (not query_major) and run.fused
         roof = {"kernel": "k_score_prefill" + (" with fused top-k" if fused_prefill else ""), "bound": "mfma",
                 "achieved": score_flops / (score_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "traffic": None, "algorithmic_flops": score_flops, "avg_ms": score_ms}
@@ -341,7 +341,7 @@ def main():
                    "query_tokens": wl.Nq, "ctx_len": wl.ctx_lens[0] if len(set(wl.ctx_lens)) == 1 else "ragged",
                    "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "Di": wl.Di, "top_k": wl.k, "block": wl.block,
                    "l2_flush_between_steps": flush is not None,
-                   "fused_index_topk": bool(not (args.two_call_topk or decode or args.prefill_mode == "query-major")),
+                   "fused_index_topk": bool(not decode and not query_major and run.fused),
                    "prefill_mode": None if decode else args.prefill_mode,
                    "kv_on_host": bool(kv_on_host),
                    "decode_select": args.decode_select if decode else None},

@@ -291,6 +291,7 @@ __global__ __launch_bounds__(256, 2) void k_score_decode_lds(
 
 constexpr int kPrefTQ = 256;  // query rows per workgroup (64 per wave)
 constexpr int kPrefSB = 16;   // blocks buffered per score flush
+constexpr int kPrefTargetWgs = 512;  // a split score launch aims for two workgroups per CU
 constexpr int kFusedTopK = 16;  // largest k the fused scorer + top-k keeps per row
 
 // Slot swizzle of the staged key-index rows: logical 16-byte chunk c of token row `row` is stored at
@@ -341,12 +342,16 @@ __device__ __forceinline__ void bitonic_sort_desc(uint64_t (&v)[N]) {
 // of both lists, a bitonic sequence) and re-sorts them with a bitonic merge.  The work is the same
 // for every row, so no lane waits on another's insertions.  The result equals msa_topk_blocks applied
 // to the written scores.
+//
+// nsplit > 1 (TOPK == 0 only): the blocks a row tile needs are cut into nsplit contiguous runs, one
+// workgroup per run, so that small problems still fill the chip.  A block's scores do not depend on
+// the run that computes them; the first run also writes the -inf tail.
 template <int DI, int TOPK>
 __global__ __launch_bounds__(256, 2) void k_score_prefill(
     int B, int Nq, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ ctx_len,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q_idx,
     const bf16* __restrict__ kidx, int Hkv, float* __restrict__ scores, int k, int32_t* __restrict__ sel,
-    int32_t* __restrict__ cnt) {
+    int32_t* __restrict__ cnt, int nsplit) {
   constexpr int KW = DI / 32;
   constexpr int BLKE = kBlock * DI;  // elements of one staged key-index block
   constexpr int CPR = DI / 8;        // 16-byte chunks per token row
@@ -359,9 +364,10 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
   int* wred = reinterpret_cast<int*>(&sbuf[0][0]);
 
   const int g = blockIdx.x % Hkv;  // consecutive workgroups take consecutive KV heads
+  const int split = (int)(blockIdx.x / Hkv) % nsplit;
   // Row tiles go from the last to the first: a request's later rows have longer causal ranges, so
   // the longest tiles start first and the short ones fill the end of the launch.
-  const int row0 = ((int)gridDim.x / Hkv - 1 - (int)blockIdx.x / Hkv) * kPrefTQ;
+  const int row0 = ((int)gridDim.x / (Hkv * nsplit) - 1 - (int)blockIdx.x / (Hkv * nsplit)) * kPrefTQ;
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, qd = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int last_row = min(row0 + kPrefTQ, Nq) - 1;
@@ -436,13 +442,16 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
             : "memory");
       }
     };
-    issue_block(0, 0);
-    for (int b0 = 0; b0 < nb; b0 += kPrefSB) {
-      const int b1 = min(b0 + kPrefSB, nb);
+    // this workgroup's run of the needed blocks (all of them unless split); uniform per workgroup
+    const int per = (nb + nsplit - 1) / nsplit;
+    const int lo = min(nb, split * per), hi = min(nb, lo + per);
+    if (lo < hi) issue_block(lo, lo & 1);
+    for (int b0 = lo; b0 < hi; b0 += kPrefSB) {
+      const int b1 = min(b0 + kPrefSB, hi);
       for (int b = b0; b < b1; ++b) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of block b are in LDS
         __syncthreads();  // every wave's are, and no wave reads the other buffer any more
-        if (b + 1 < nb) issue_block(b + 1, (b & 1) ^ 1);
+        if (b + 1 < hi) issue_block(b + 1, (b & 1) ^ 1);
         const bf16* kbuf = ks[b & 1];
         // operand of 16-token tile mt, k window kw for lane (n, qd): row 16mt + n, logical chunk 4kw + qd
         auto frag = [&](int mt, int kw) {
@@ -517,8 +526,8 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
       }
     }
     if constexpr (TOPK == 0) {
-      // non-candidate tail
-      const int tail = max_blocks - nb;
+      // non-candidate tail, written by the first run
+      const int tail = split == 0 ? max_blocks - nb : 0;
       for (int e = tid; e < (qb - qa) * tail; e += 256) {
         const int row = qa + e / tail, b = nb + e % tail;
         scores[((int64_t)row * Hkv + g) * max_blocks + b] = neg_inf();
@@ -576,15 +585,19 @@ hipError_t launch_score_prefill(int B, int Nq, int Di, const int32_t* block_tabl
                                 const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const void* q_idx,
                                 const void* kidx, int Hkv, float* scores, hipStream_t stream) {
   const int tiles = (Nq + kPrefTQ - 1) / kPrefTQ;
-  dim3 grid(tiles * Hkv), block(256);
+  // Few row tiles (short prompts): cut each tile's blocks into runs of two or more blocks, doubling
+  // the runs while the launch stays within kPrefTargetWgs workgroups.
+  int nsplit = 1;
+  while ((int64_t)tiles * Hkv * nsplit * 2 <= kPrefTargetWgs && nsplit * 4 <= max_blocks) nsplit *= 2;
+  dim3 grid(tiles * Hkv * nsplit), block(256);
   const bf16* qi = static_cast<const bf16*>(q_idx);
   const bf16* ki = static_cast<const bf16*>(kidx);
   if (Di == 128)
     hipLaunchKernelGGL((k_score_prefill<128, 0>), grid, block, 0, stream, B, Nq, block_table, max_blocks, ctx_len,
-                       cu_q, q_pos, qi, ki, Hkv, scores, 0, nullptr, nullptr);
+                       cu_q, q_pos, qi, ki, Hkv, scores, 0, nullptr, nullptr, nsplit);
   else
     hipLaunchKernelGGL((k_score_prefill<64, 0>), grid, block, 0, stream, B, Nq, block_table, max_blocks, ctx_len,
-                       cu_q, q_pos, qi, ki, Hkv, scores, 0, nullptr, nullptr);
+                       cu_q, q_pos, qi, ki, Hkv, scores, 0, nullptr, nullptr, nsplit);
   return hipGetLastError();
 }
 
@@ -600,10 +613,10 @@ hipError_t launch_score_topk_prefill(int B, int Nq, int Di, const int32_t* block
   const bf16* ki = static_cast<const bf16*>(kidx);
   if (Di == 128)
     hipLaunchKernelGGL((k_score_prefill<128, kFusedTopK>), grid, block, 0, stream, B, Nq, block_table, max_blocks,
-                       ctx_len, cu_q, q_pos, qi, ki, Hkv, nullptr, k, sel, cnt);
+                       ctx_len, cu_q, q_pos, qi, ki, Hkv, nullptr, k, sel, cnt, 1);
   else
     hipLaunchKernelGGL((k_score_prefill<64, kFusedTopK>), grid, block, 0, stream, B, Nq, block_table, max_blocks,
-                       ctx_len, cu_q, q_pos, qi, ki, Hkv, nullptr, k, sel, cnt);
+                       ctx_len, cu_q, q_pos, qi, ki, Hkv, nullptr, k, sel, cnt, 1);
   return hipGetLastError();
 }
 

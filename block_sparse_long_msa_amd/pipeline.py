@@ -81,17 +81,24 @@ class MSADecode:
 
 
 class MSAPrefill:
-    """``fused=True`` (the default) scores and selects in one call (msa_index_topk): for k <= 16 the
-    block scores never reach memory and ``scores`` is not kept; on the long-prefill workload this is
-    faster than the two calls.  ``fused=False`` runs msa_index_score then msa_topk_blocks and keeps the
-    scores."""
+    """``fused=True`` scores and selects in one call (msa_index_topk): for k <= 16 the block scores
+    never reach memory and ``scores`` is not kept; on the long-prefill workload this is faster than
+    the two calls.  ``fused=False`` runs msa_index_score then msa_topk_blocks and keeps the scores.
+    ``fused=None`` (the default) takes the fused call when its launch fills the chip, i.e. has at
+    least ``FUSED_MIN_WGS`` workgroups (one per 256 query rows and KV head); shorter chunks take the
+    two calls, whose scorer splits each row tile's blocks over several workgroups."""
+
+    ROW_TILE = 256        # query rows per workgroup of the prefill scorer
+    FUSED_MIN_WGS = 256   # half of the two workgroups per CU the scorer runs at
 
     def __init__(self, batch: Batch, Hkv: int, G: int, D: int, k: int, num_pages: int, device="cuda",
-                 fused: bool = True):
+                 fused=None):
         Nq, mb = batch.num_queries, batch.max_blocks
         self.batch, self.Hkv, self.G, self.D, self.k, self.num_pages = batch, Hkv, G, D, k, num_pages
-        self.fused = fused
-        self.scores = None if fused else torch.empty((Nq, Hkv, mb), dtype=torch.float32, device=device)
+        if fused is None:
+            fused = -(-Nq // self.ROW_TILE) * Hkv >= self.FUSED_MIN_WGS
+        self.fused = bool(fused)
+        self.scores = None if self.fused else torch.empty((Nq, Hkv, mb), dtype=torch.float32, device=device)
         self.topk_ws = torch.empty((max(1, msa_index_topk_workspace_size(batch, Hkv, k)),), dtype=torch.uint8,
                                    device=device)
         self.sel = torch.empty((Nq, Hkv, k), dtype=torch.int32, device=device)
