@@ -91,13 +91,16 @@ class MSAPrefill:
     ROW_TILE = 256        # query rows per workgroup of the prefill scorer
     FUSED_MIN_WGS = 256   # half of the two workgroups per CU the scorer runs at
 
+    @classmethod
+    def prefers_fused(cls, num_queries: int, Hkv: int) -> bool:
+        """The default route: the fused call when its launch has FUSED_MIN_WGS workgroups or more."""
+        return -(-num_queries // cls.ROW_TILE) * Hkv >= cls.FUSED_MIN_WGS
+
     def __init__(self, batch: Batch, Hkv: int, G: int, D: int, k: int, num_pages: int, device="cuda",
                  fused=None):
         Nq, mb = batch.num_queries, batch.max_blocks
         self.batch, self.Hkv, self.G, self.D, self.k, self.num_pages = batch, Hkv, G, D, k, num_pages
-        if fused is None:
-            fused = -(-Nq // self.ROW_TILE) * Hkv >= self.FUSED_MIN_WGS
-        self.fused = bool(fused)
+        self.fused = self.prefers_fused(Nq, Hkv) if fused is None else bool(fused)
         self.scores = None if self.fused else torch.empty((Nq, Hkv, mb), dtype=torch.float32, device=device)
         self.topk_ws = torch.empty((max(1, msa_index_topk_workspace_size(batch, Hkv, k)),), dtype=torch.uint8,
                                    device=device)
