@@ -585,10 +585,10 @@ hipError_t launch_score_prefill(int B, int Nq, int Di, const int32_t* block_tabl
                                 const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const void* q_idx,
                                 const void* kidx, int Hkv, float* scores, hipStream_t stream) {
   const int tiles = (Nq + kPrefTQ - 1) / kPrefTQ;
-  // Few row tiles (short prompts): cut each tile's blocks into runs of two or more blocks, doubling
-  // the runs while the launch stays within kPrefTargetWgs workgroups.
+  // Few row tiles (short prompts): cut each tile's blocks into runs, doubling the runs while the
+  // launch stays within kPrefTargetWgs workgroups and there are blocks for every run.
   int nsplit = 1;
-  while ((int64_t)tiles * Hkv * nsplit * 2 <= kPrefTargetWgs && nsplit * 4 <= max_blocks) nsplit *= 2;
+  while ((int64_t)tiles * Hkv * nsplit * 2 <= kPrefTargetWgs && nsplit * 2 <= max_blocks) nsplit *= 2;
   dim3 grid(tiles * Hkv * nsplit), block(256);
   const bf16* qi = static_cast<const bf16*>(q_idx);
   const bf16* ki = static_cast<const bf16*>(kidx);
