@@ -429,8 +429,8 @@ __global__ __launch_bounds__(256) void k_lse_merge(int64_t rows, int parts, int 
       const float lj = pl[j * G + lane];
       w[j * G + lane] = lj == neg_inf() ? 0.f : __expf(lj - M) * inv;
     }
-    s_lse[wv][lane] = M + __logf(den);
-    s_first[wv][lane] = first;
+    s_lse[wv][lane] = M + __logf(den);  // -inf when no part is present
+    s_first[wv][lane] = max(first, 0);  // no present part: every weight is 0, reads stay in the row
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");

@@ -523,7 +523,8 @@ __global__ __launch_bounds__(kThreads, MSA_KVBM_OCC) void k_attn_kvbm(
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       const int rr = 16 * nt + n, h = rr % G;
-      const int t = tj[nt] >> 6, j = tj[nt] & 63;
+      const int tjc = max(tj[nt], 0);  // padded rows (tj = -1) are never stored; keep their slot in range
+      const int t = tjc >> 6, j = tjc & 63;
       orow[nt] = (((int64_t)t * Hkv + g) * k + j) * G + h;
       inv[nt] = __builtin_amdgcn_rcpf(lrow[nt]);
       if (tj[nt] >= 0 && qd == 0) part_lse[orow[nt]] = (mrow[nt] + fast_log2(lrow[nt])) * kLn2P;

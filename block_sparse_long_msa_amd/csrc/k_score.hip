@@ -228,6 +228,9 @@ __global__ __launch_bounds__(256, 2) void k_score_decode_lds(
     u32x4 regs[2][LPT];
     load_slice(regs[0], 0);
     load_slice(regs[1], 1);
+    // a request with more than 16 queries runs this loop again: the previous chunk's last slices
+    // may still be read from both stage buffers by slower waves
+    if (qc > 0) __syncthreads();
     store_slice(regs[0], 0);
     load_slice(regs[0], 2);
     __syncthreads();

@@ -195,7 +195,8 @@ size_t msa_sparse_attn_prefill_workspace_size(const msa_batch* batch, int32_t nu
 
 /* Log-sum-exp reduction of per-block partials (section "KV块主序稀疏注意力减少冗余KV移动"):
  *   LSE = log sum_j exp(lse_j),  O = sum_j exp(lse_j - LSE) * O_j, over the parts with
- *   lse_j > -inf (at least one per row and head).
+ *   lse_j > -inf.  A (row, head) with no such part gets O = 0 and LSE = -inf (every read stays
+ *   inside the row's own parts).
  *   part_o    device bf16 [rows, parts, G, D];  part_lse  device f32 [rows, parts, G]
  *   out       device bf16 [rows, G, D];         lse_out   device f32 [rows, G] or NULL */
 msa_status msa_lse_merge(int64_t rows, int32_t parts, int32_t G, int32_t D, const void* part_o,

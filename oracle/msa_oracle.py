@@ -132,15 +132,6 @@ def attend(qv, keys, vals, scale):
     return (w @ vals) / s, m + math.log(s)
 
 
-def selected_token_ids(sel_row, cnt, pos, L, block):
-    """Logical token ids of the valid tokens of the selected blocks, in selection order."""
-    ids = []
-    for b in sel_row[:cnt]:
-        n = valid_token_count(int(b), pos, L, block)
-        ids.extend(range(int(b) * block, int(b) * block + n))
-    return np.asarray(ids, dtype=np.int64)
-
-
 def selected_kv(kcache, vcache, block_table_row, sel_row, cnt, g, pos, L, block):
     """Keys and values [n, D] of the valid tokens of the selected blocks of KV head g, in
     selection order (gathered page by page through the block table)."""

@@ -50,11 +50,27 @@ def test_index_topk_equals_score_then_topk(name):
     msa.msa_index_topk(b, dev.q_idx, dev.kidx, wl.k, sel_b, cnt_b, ws)
     sa, ca, sb, cb = host(sel_a), host(cnt_a), host(sel_b), host(cnt_b)
     assert np.array_equal(sa, sb) and np.array_equal(ca, cb)
+    # strictly, with no excusal: the oracle's top-k on the GPU's own fp32 scores decides every exact tie
+    # at the k-th boundary by the lower block id (tied_blocks_k16 has such ties on many rows)
+    o_sel, o_cnt = oracle.topk_blocks(host(s).astype(np.float64), host(dev.q_pos), wl.block, wl.k)
+    assert np.array_equal(sa, o_sel) and np.array_equal(ca, o_cnt), "msa_topk_blocks breaks the tie rule"
+    assert np.array_equal(sb, o_sel) and np.array_equal(cb, o_cnt), "msa_index_topk breaks the tie rule"
+    if name == "tied_blocks_k16":
+        assert _boundary_ties(host(s), wl.k) >= 50, "the tie case lost its exact ties at the k-th boundary"
     # and against the oracle's own scores (boundary-excused)
     x = np_inputs(cpu)
     ref_s = oracle.index_scores(x.q_idx, x.kidx, x.block_table, x.ctx_len, x.q_req, x.q_pos, wl.block)
     r_sel, r_cnt = oracle.topk_blocks(ref_s, x.q_pos, wl.block, wl.k)
     selection_excused(sb, cb, r_sel, r_cnt, ref_s, wl.k)
+
+
+def _boundary_ties(s, k):
+    """Rows (t, g) whose k-th and (k+1)-th best scores are exactly equal."""
+    n = 0
+    for row in s.reshape(-1, s.shape[-1]):
+        f = np.sort(row[np.isfinite(row)])[::-1]
+        n += int(len(f) > k and f[k - 1] == f[k])
+    return n
 
 
 def test_fused_route_has_no_workspace():
