@@ -15,7 +15,7 @@ from ._lib import EXPORTS, MsaBatch, MsaCache, MSAError, check, load  # noqa: F4
 
 __all__ = ["Batch", "HostResident", "MSAError", "msa_index_score", "msa_index_topk", "msa_index_topk_workspace_size",
            "msa_topk_blocks", "msa_build_sparse_page_table", "msa_topk_page_table", "msa_topk_attn_decode",
-           "msa_sparse_attn_decode", "msa_sparse_attn_decode_workspace_size", "msa_sparse_attn_prefill",
+           "msa_topk_attn_decode_noalloc", "msa_sparse_attn_decode", "msa_sparse_attn_decode_workspace_size", "msa_sparse_attn_prefill",
            "msa_sparse_attn_prefill_workspace_size", "msa_lse_merge", "msa_version", "load"]
 
 
@@ -170,6 +170,18 @@ def msa_topk_attn_decode(batch: Batch, scores, k: int, k_cache, v_cache, G: int,
                                       _ptr(lse, torch.float32, "lse", True),
                                       _ptr(workspace, torch.uint8, "workspace", True),
                                       0 if workspace is None else workspace.numel(), _stream(stream)))
+
+
+def msa_topk_attn_decode_noalloc(batch: Batch, scores, k: int, k_cache, v_cache, G: int, q, sm_scale: float, sel,
+                                 cnt, page_table, row_len, out, lse, stream=None) -> None:
+    check("msa_topk_attn_decode_noalloc",
+          load().msa_topk_attn_decode_noalloc(batch.ref(), _ptr(scores, torch.float32, "scores"), k,
+                                              _cache(k_cache, "k_cache"), _cache(v_cache, "v_cache"), G,
+                                              _ptr(q, torch.bfloat16, "q"), sm_scale, _ptr(sel, torch.int32, "sel"),
+                                              _ptr(cnt, torch.int32, "cnt"),
+                                              _ptr(page_table, torch.int32, "page_table"),
+                                              _ptr(row_len, torch.int32, "row_len"), _ptr(out, torch.bfloat16, "out"),
+                                              _ptr(lse, torch.float32, "lse", True), _stream(stream)))
 
 
 def msa_sparse_attn_decode_workspace_size(rows: int, G: int, D: int, k: int) -> int:

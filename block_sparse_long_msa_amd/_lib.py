@@ -14,7 +14,7 @@ MSA_STATUS = {0: "MSA_OK", 1: "MSA_ERR_INVALID_ARG", 2: "MSA_ERR_UNSUPPORTED", 3
 
 # Every symbol include/msa.h declares.
 EXPORTS = ("msa_index_score", "msa_index_topk", "msa_index_topk_workspace_size", "msa_topk_blocks", "msa_build_sparse_page_table",
-           "msa_topk_page_table", "msa_topk_attn_decode", "msa_sparse_attn_decode",
+           "msa_topk_page_table", "msa_topk_attn_decode", "msa_topk_attn_decode_noalloc", "msa_sparse_attn_decode",
            "msa_sparse_attn_decode_workspace_size", "msa_sparse_attn_prefill",
            "msa_sparse_attn_prefill_workspace_size", "msa_lse_merge", "msa_status_string", "msa_last_error",
            "msa_version")
@@ -42,6 +42,8 @@ _SIGS = {
                                     c_vp]),
     "msa_topk_attn_decode": (c_i32, [ctypes.POINTER(MsaBatch), c_vp, c_i32, MsaCache, MsaCache, c_i32, c_vp, c_f32,
                                      c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "msa_topk_attn_decode_noalloc": (c_i32, [ctypes.POINTER(MsaBatch), c_vp, c_i32, MsaCache, MsaCache, c_i32, c_vp,
+                                             c_f32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "msa_sparse_attn_decode": (c_i32, [c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_f32,
                                        c_vp, c_vp, c_vp, c_size, c_vp]),
     "msa_sparse_attn_decode_workspace_size": (c_size, [c_i32, c_i32, c_i32, c_i32]),

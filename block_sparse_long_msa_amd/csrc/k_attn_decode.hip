@@ -21,7 +21,9 @@
 // k_lse_merge: LSE = log sum_j exp(lse_j); O = sum_j exp(lse_j - LSE) O_j over the parts with
 //   lse_j > -inf (section "KV块主序稀疏注意力减少冗余KV移动").
 #include <algorithm>
+#include <mutex>
 
+#include "msa.h"
 #include "msa_device.h"
 #include "topk_select.h"
 
@@ -563,6 +565,37 @@ hipError_t launch_select_attend(int B, int Nq, int Hkv, int max_blocks, const in
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
   return launch_merge_splits(rows, G, D, nsplit, ws_o, ws_lse, oo, lse, stream);
+}
+
+// Split partials of msa_topk_attn_decode_noalloc, for callers that cannot allocate device memory.
+// One copy of this array lives on every GPU the library runs on, for the life of the process.  Every
+// split writes its own LSE (-inf for a split past its row's last page) before the merge reads it, and
+// an absent split is read from split 0 with weight 0, so nothing has to be cleared between calls.
+constexpr size_t kDecodeScratchBytes = MSA_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+constexpr int kMaxDevices = 64;
+
+size_t decode_scratch_bytes() { return kDecodeScratchBytes; }
+
+// Device address of the current device's copy of `scratch`, looked up once per device with that
+// device current.  In host code the array's name is only a host-side stand-in, never a device address.
+hipError_t decode_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_lse_merge_bf16(int64_t rows, int parts, int G, int D, const void* part_o, const float* part_lse,

@@ -42,6 +42,8 @@ hipError_t launch_attn_decode(int rows, int G, int D, const void* q, const void*
                               float* ws_lse, hipStream_t stream);
 hipError_t launch_lse_merge_bf16(int64_t rows, int parts, int G, int D, const void* part_o, const float* part_lse,
                                  void* out, float* lse_out, hipStream_t stream);
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** ptr);
 size_t prefill_workspace_bytes(int32_t Nq, int32_t Hkv, int32_t k, int32_t B, int32_t max_blocks);
 hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blocks, const int32_t* block_table,
                                const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const void* q,
@@ -297,10 +299,14 @@ msa_status msa_sparse_attn_decode(int32_t rows, int32_t G, int32_t D, const void
                   "msa_sparse_attn_decode launch");
 }
 
-msa_status msa_topk_attn_decode(const msa_batch* batch, const float* scores, int32_t k, msa_cache k_cache,
-                                msa_cache v_cache, int32_t G, const void* q, float sm_scale, int32_t* sel, int32_t* cnt,
-                                int32_t* page_table, int32_t* row_len, void* out, float* lse, void* workspace,
-                                size_t workspace_bytes, msa_stream_t stream) {
+namespace {
+
+// msa_topk_attn_decode and its allocation-free form: the same checks and launches; the split partials
+// go to the caller's workspace, or (use_scratch) to the library's static per-device scratch.
+msa_status topk_attn_decode(const msa_batch* batch, const float* scores, int32_t k, msa_cache k_cache,
+                            msa_cache v_cache, int32_t G, const void* q, float sm_scale, int32_t* sel, int32_t* cnt,
+                            int32_t* page_table, int32_t* row_len, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, bool use_scratch, msa_stream_t stream) {
   g_last_error.clear();
   if (msa_status s = check_batch(batch)) return s;
   if (msa_status s = check_cache(k_cache, "k_cache")) return s;
@@ -325,8 +331,19 @@ msa_status msa_topk_attn_decode(const msa_batch* batch, const float* scores, int
               MSA_ERR_INVALID_ARG, "scores, sel, cnt, page_table, row_len and lse must be 4-byte aligned");
   const int rows = (int)rows64;
   const size_t need = msa_sparse_attn_decode_workspace_size(rows, G, D, k);
-  MSA_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), MSA_ERR_WORKSPACE_TOO_SMALL,
-              "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  if (use_scratch) {
+    MSA_REQUIRE(need <= msa::decode_scratch_bytes(), MSA_ERR_UNSUPPORTED,
+                "this batch needs %zu bytes of split scratch, more than the %zu bytes the allocation-free entry "
+                "point holds; call msa_topk_attn_decode with a workspace instead",
+                need, msa::decode_scratch_bytes());
+    if (need > 0) {
+      if (msa_status s = from_hip(msa::decode_scratch(&workspace), "msa_topk_attn_decode_noalloc scratch lookup"))
+        return s;
+    }
+  } else {
+    MSA_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), MSA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace needs %zu bytes, got %zu", need, workspace_bytes);
+  }
   const size_t parts = (size_t)rows * msa::decode_splits(rows, k) * G;
   float* ws_o = static_cast<float*>(workspace);
   float* ws_lse = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(parts * D * sizeof(float)))
@@ -346,6 +363,24 @@ msa_status msa_topk_attn_decode(const msa_batch* batch, const float* scores, int
   return from_hip(msa::launch_attn_decode(rows, G, D, q, k_cache.data, v_cache.data, D, (int64_t)Hkv * D, page_table,
                                           k, row_len, sm_scale, out, lse, ws_o, ws_lse, st),
                   "msa_topk_attn_decode attention launch");
+}
+
+}  // namespace
+
+msa_status msa_topk_attn_decode(const msa_batch* batch, const float* scores, int32_t k, msa_cache k_cache,
+                                msa_cache v_cache, int32_t G, const void* q, float sm_scale, int32_t* sel, int32_t* cnt,
+                                int32_t* page_table, int32_t* row_len, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, msa_stream_t stream) {
+  return topk_attn_decode(batch, scores, k, k_cache, v_cache, G, q, sm_scale, sel, cnt, page_table, row_len, out, lse,
+                          workspace, workspace_bytes, false, stream);
+}
+
+msa_status msa_topk_attn_decode_noalloc(const msa_batch* batch, const float* scores, int32_t k, msa_cache k_cache,
+                                        msa_cache v_cache, int32_t G, const void* q, float sm_scale, int32_t* sel,
+                                        int32_t* cnt, int32_t* page_table, int32_t* row_len, void* out, float* lse,
+                                        msa_stream_t stream) {
+  return topk_attn_decode(batch, scores, k, k_cache, v_cache, G, q, sm_scale, sel, cnt, page_table, row_len, out, lse,
+                          nullptr, 0, true, stream);
 }
 
 size_t msa_sparse_attn_prefill_workspace_size(const msa_batch* batch, int32_t num_kv_heads, int32_t k) {

@@ -172,6 +172,22 @@ msa_status msa_topk_attn_decode(const msa_batch* batch, const float* scores, int
                                 int32_t* cnt, int32_t* page_table, int32_t* row_len, void* out, float* lse,
                                 void* workspace, size_t workspace_bytes, msa_stream_t stream);
 
+/* msa_topk_attn_decode for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments, outputs and results as
+ * msa_topk_attn_decode, with no workspace: when rows have to be split over several workgroups, the split
+ * partials go to a static array of MSA_DECODE_NOALLOC_SCRATCH_BYTES bytes that the library holds on each
+ * GPU it runs on until the process ends.  This call allocates nothing (no hipMalloc, no library
+ * allocation).  A batch whose split partials need more than that (msa_sparse_attn_decode_workspace_size
+ * of Nq*Hkv rows above the limit: at most 16 query heads per KV head, D = 128 and close to 256 rows)
+ * returns MSA_ERR_UNSUPPORTED and launches nothing.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (different streams without ordering between them) race and give
+ * undefined results; calls on one stream, or ordered by events, are safe. */
+#define MSA_DECODE_NOALLOC_SCRATCH_BYTES (4u << 20)
+msa_status msa_topk_attn_decode_noalloc(const msa_batch* batch, const float* scores, int32_t k, msa_cache k_cache,
+                                        msa_cache v_cache, int32_t G, const void* q, float sm_scale, int32_t* sel,
+                                        int32_t* cnt, int32_t* page_table, int32_t* row_len, void* out, float* lse,
+                                        msa_stream_t stream);
+
 /* KV-block-major prefill attention (section "KV块主序稀疏注意力减少冗余KV移动"; Russian page,
  * third paragraph): the selection is inverted into {(KV head, physical page) -> queries}
  * lists, each selected KV block is staged on chip and attended by every query row that

@@ -149,6 +149,23 @@ def test_topk_attn_decode_rejects_null_outputs(lib):
 
 
 @no_gpu
+def test_topk_attn_decode_noalloc_rejects_batches_beyond_its_scratch(lib):
+    # 51 queries x 5 KV heads = 255 rows of 16 query heads at D = 128, split in two: 4,210,688 bytes of
+    # partials, more than the 4 MiB static scratch
+    b = _batch(B=51, Nq=51)
+    kc = _cache(H=5, D=128)
+    assert lib.msa_sparse_attn_decode_workspace_size(255, 16, 128, 64) > (4 << 20)
+    st = lib.msa_topk_attn_decode_noalloc(ctypes.byref(b), FAKE, 64, kc, kc, 16, FAKE, 0.1, FAKE, FAKE, FAKE, FAKE,
+                                          FAKE, FAKE, None)
+    assert st == UNSUPPORTED and b"allocation-free" in lib.msa_last_error()
+    assert lib.msa_topk_attn_decode_noalloc(ctypes.byref(b), FAKE, 65, kc, kc, 16, FAKE, 0.1, FAKE, FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, None) == UNSUPPORTED
+    e = _batch(Nq=0)
+    assert lib.msa_topk_attn_decode_noalloc(ctypes.byref(e), None, 4, _cache(), _cache(), 8, None, 0.1, None, None,
+                                            None, None, None, None, None) == OK
+
+
+@no_gpu
 def test_prefill_attention_rejects(lib):
     b = _batch(Nq=40, maxq=40)
     kc, vc = _cache(), _cache()
