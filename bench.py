@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--kv-on-host", action="store_true",
                    help="decode: keep the key-index cache in HBM but move the K/V caches to pinned host memory; "
                         "attention then reads only the selected blocks over the host link")
+    p.add_argument("--no-suite", action="store_true",
+                   help="time only --workload (by default the other workloads follow, each timed the same way, and "
+                        "their per-kernel lines go under 'suite')")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, run one plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -126,8 +129,10 @@ def cpu_baseline(dev, budget_s: float):
     """Time the CPU oracle (as it stands) on whole query rows of this workload until about
     ``budget_s`` seconds of oracle time are spent, going over the workload again when one pass is
     shorter than that.  Per sampled request the oracle sees only that request's pages, copied to
-    host memory outside the timed sections.  BLAS gets every core this process may run on (capped
-    by OMP_NUM_THREADS when that is set): the oracle's time is mostly in its NumPy products."""
+    host memory outside the timed sections.  The oracle loops over query rows, blocks and heads in
+    Python, and each step is a small NumPy product (one 128-token block against one query vector), so
+    its time goes to those loops and call overheads, not to BLAS throughput: it runs on one core with
+    one BLAS thread, and ``cores`` says so."""
     from threadpoolctl import threadpool_limits
 
     import oracle
@@ -138,10 +143,7 @@ def cpu_baseline(dev, budget_s: float):
     decode = max(wl.q_counts) <= 16
     spent, tokens, sampled, passes = 0.0, 0, [], 0
     kidx_host = {}                                                          # request -> its K-index pages
-    threads = len(os.sched_getaffinity(0))
-    omp = os.environ.get("OMP_NUM_THREADS", "")
-    if omp.isdigit() and int(omp) > 0:
-        threads = min(threads, int(omp))
+    threads = 1
     with threadpool_limits(limits=threads):
         while spent < budget_s:
             passes += 1
@@ -196,20 +198,17 @@ def cpu_baseline(dev, budget_s: float):
             "oracle_s": spent}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the MSA path would shard "
-              "by request or KV head with no exchange; only the one-GPU share is built and timed)",
-              file=sys.stderr)
-        sys.exit(2)
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
+SUITE = (("tiny_prefill", None), ("long_prefill", None), ("million_decode", 1), ("million_decode", 4),
+         ("ragged_decode", None), ("spec_decode", None))
+
+
+def measure(args, name, batch):
+    """Time one workload: W warm-up steps, then K steps bracketed by HIP events, a 1 GiB read before
+    every step.  Returns (summary dict, inputs, pipeline)."""
     import block_sparse_long_msa_amd as msa
     from block_sparse_long_msa_amd.pipeline import MSADecode, MSAPrefill, MSAPrefillQueryMajor
-    msa.load()
-    torch.cuda.set_device(0)
 
-    wl = make_workload(args.workload, args.batch)
+    wl = make_workload(name, batch)
     decode = max(wl.q_counts) <= 16
     t0 = time.time()
     dev = mi.make_inputs(wl, "cuda")
@@ -243,16 +242,16 @@ def main():
               ["score", "select", "attend"] + ([] if decode or query_major else ["merge"]))
 
     def step(evs=None):
-        for i, name in enumerate(stages):
+        for i, stage in enumerate(stages):
             if evs is not None:
                 evs[i].record()
-            if name == "score":
+            if stage == "score":
                 run.score(dev.q_idx, dev.kidx)
-            elif name == "select":
+            elif stage == "select":
                 run.select()
-            elif name == "attend":
+            elif stage == "attend":
                 run.attend(dev.q, kv_k, kv_v, dev.scale)
-            elif name == "select_attend":
+            elif stage == "select_attend":
                 run.select_attend(dev.q, kv_k, kv_v, dev.scale)
             else:
                 run.merge()
@@ -278,8 +277,7 @@ def main():
                           for i in range(args.steps)])                     # ms
     step_ms = per_stage.sum(axis=1)
     ms_per_step = float(step_ms.mean())
-    tokens = wl.Nq
-    value = tokens / (ms_per_step / 1e3)
+    value = wl.Nq / (ms_per_step / 1e3)
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -287,7 +285,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    # roofline of the scorer (dominant kernel) and of the attention kernel
+    # roofline of the scorer and of the attention (and merge) kernels
     score_ms = float(per_stage[:, 0].mean())
     attend_ms = float(per_stage[:, stages.index("select_attend" if fused_decode else "attend")].mean())
     cand = candidate_tokens(wl)
@@ -323,20 +321,14 @@ def main():
     details = [roof, roof_attn]
     if not decode and not query_major:
         merge_ms = float(per_stage[:, 3].mean())
-        merge_bytes = (run.part_o.numel() * 2 + run.part_lse.numel() * 4 + run.out.numel() * 2 + run.lse.numel() * 4)
+        merge_bytes = run.merge_bytes()
         details.append({"kernel": "k_lse_merge<bf16>", "bound": "hbm", "achieved": merge_bytes / (merge_ms * 1e-3) / 1e9,
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "algorithmic_bytes": merge_bytes, "avg_ms": merge_ms})
     for r in details:
         r["frac"] = r["achieved"] / r["peak"]
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(dev, budget_s=args.cpu_budget_s)
-
-    line = {
-        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+    summary = {
+        "workload": wl.name, "phase": "decode" if decode else "prefill", "tokens_per_s": value,
+        "ms_per_step": ms_per_step,
         "config": {"workload": wl.name, "phase": "decode" if decode else "prefill", "requests": wl.B,
                    "query_tokens": wl.Nq, "ctx_len": wl.ctx_lens[0] if len(set(wl.ctx_lens)) == 1 else "ragged",
                    "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "Di": wl.Di, "top_k": wl.k, "block": wl.block,
@@ -345,12 +337,61 @@ def main():
                    "prefill_mode": None if decode else args.prefill_mode,
                    "kv_on_host": bool(kv_on_host),
                    "decode_select": args.decode_select if decode else None},
-        "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
         "roofline_detail": details,
-        "stage_ms": {name: float(per_stage[:, i].mean()) for i, name in enumerate(stages)},
+        "stage_ms": {stage: float(per_stage[:, i].mean()) for i, stage in enumerate(stages)},
         "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
-        "cpu_baseline": cpu,
         "wall_s_timed": wall, "input_gen_s": gen_s,
+    }
+    return summary, dev, run
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the MSA path would shard "
+              "by request or KV head with no exchange; only the one-GPU share is built and timed)",
+              file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import block_sparse_long_msa_amd as msa
+    msa.load()
+    torch.cuda.set_device(0)
+
+    head, dev, run = measure(args, args.workload, args.batch)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(dev, budget_s=args.cpu_budget_s)
+    del dev, run
+    torch.cuda.empty_cache()
+
+    # the other workloads of the same metric, each timed the same way in this run
+    suite = []
+    if not args.no_suite:
+        for name, batch in SUITE:
+            if name == args.workload and (batch or 1) == (args.batch or 1):
+                continue
+            s, dev, run = measure(args, name, batch)
+            suite.append({k: s[k] for k in ("workload", "phase", "tokens_per_s", "ms_per_step", "stage_ms",
+                                             "roofline_detail", "input_gen_s")})
+            print(f"# {s['workload']}: {s['ms_per_step']:.3f} ms per step, "
+                  + ", ".join(f"{r['kernel']} {r['frac']:.3f}" for r in s["roofline_detail"]),
+                  file=sys.stderr, flush=True)
+            del dev, run
+            torch.cuda.empty_cache()
+
+    roof = head["roofline_detail"][0]
+    line = {
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": head["config"],
+        "roofline": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "roofline_detail": head["roofline_detail"],
+        "stage_ms": head["stage_ms"],
+        "step_ms_p10_p50_p90": head["step_ms_p10_p50_p90"],
+        "cpu_baseline": cpu,
+        "wall_s_timed": head["wall_s_timed"], "input_gen_s": head["input_gen_s"],
+        "suite": suite,
     }
     print(json.dumps(line), flush=True)
 

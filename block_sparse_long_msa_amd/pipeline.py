@@ -131,6 +131,10 @@ class MSAPrefill:
         rows = self.batch.num_queries * self.Hkv
         msa_lse_merge(rows, self.k, self.G, self.D, self.part_o, self.part_lse, self.out, self.lse, stream)
 
+    def merge_bytes(self) -> int:
+        """Bytes the merge moves: every part slot's partial and LSE in, the outputs out."""
+        return (self.part_o.numel() * 2 + self.part_lse.numel() * 4 + self.out.numel() * 2 + self.lse.numel() * 4)
+
     def __call__(self, q, q_idx, kcache, vcache, kidx, sm_scale: float, stream=None):
         self.score(q_idx, kidx, stream)
         self.select(stream)
