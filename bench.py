@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--two-call-topk", action="store_true",
                    help="prefill: always score and select with msa_index_score then msa_topk_blocks (by "
                         "default the fused msa_index_topk runs whenever its launch fills the chip)")
+    p.add_argument("--tile-min-rows", type=int, default=None,
+                   help="prefill: merge each row's blocks that at least this many rows picked in query tiles "
+                        "(0: one partial per selected block; default: the pipeline's)")
     p.add_argument("--prefill-mode", default="kvbm", choices=["kvbm", "query-major"],
                    help="prefill attention: KV-block-major with LSE merge (the method), or the query-major "
                         "baseline it is measured against (each row reads its own blocks)")
@@ -227,7 +230,8 @@ def measure(args, name, batch):
     elif query_major:
         run = MSAPrefillQueryMajor(b, wl.Hkv, wl.G, wl.D, wl.k, P)
     else:
-        run = MSAPrefill(b, wl.Hkv, wl.G, wl.D, wl.k, P, fused=False if args.two_call_topk else None)
+        run = MSAPrefill(b, wl.Hkv, wl.G, wl.D, wl.k, P, fused=False if args.two_call_topk else None,
+                         tile_min_rows=args.tile_min_rows)
     flush = None
     if not args.no_flush:
         flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -335,6 +339,7 @@ def measure(args, name, batch):
                    "l2_flush_between_steps": flush is not None,
                    "fused_index_topk": bool(not decode and not query_major and run.fused),
                    "prefill_mode": None if decode else args.prefill_mode,
+                   "tile_min_rows": None if decode or query_major else run.tile_min_rows,
                    "kv_on_host": bool(kv_on_host),
                    "decode_select": args.decode_select if decode else None},
         "roofline_detail": details,

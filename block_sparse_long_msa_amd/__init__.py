@@ -205,13 +205,14 @@ def msa_sparse_attn_prefill_workspace_size(batch: Batch, num_kv_heads: int, k: i
 
 
 def msa_sparse_attn_prefill(batch: Batch, G: int, q, k_cache, v_cache, sel, cnt, k: int, sm_scale: float, part_o,
-                            part_lse, workspace, stream=None) -> None:
+                            part_lse, workspace, stream=None, tile_min_rows: int = 0, slot_of=None) -> None:
     check("msa_sparse_attn_prefill",
           load().msa_sparse_attn_prefill(batch.ref(), G, _ptr(q, torch.bfloat16, "q"), _cache(k_cache, "k_cache"),
                                          _cache(v_cache, "v_cache"), _ptr(sel, torch.int32, "sel"),
-                                         _ptr(cnt, torch.int32, "cnt"), k, sm_scale,
+                                         _ptr(cnt, torch.int32, "cnt"), k, sm_scale, tile_min_rows,
                                          _ptr(part_o, torch.bfloat16, "part_o"),
                                          _ptr(part_lse, torch.float32, "part_lse"),
+                                         _ptr(slot_of, torch.int32, "slot_of", True),
                                          _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                                          _stream(stream)))
 

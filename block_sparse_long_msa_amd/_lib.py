@@ -48,7 +48,7 @@ _SIGS = {
                                        c_vp, c_vp, c_vp, c_size, c_vp]),
     "msa_sparse_attn_decode_workspace_size": (c_size, [c_i32, c_i32, c_i32, c_i32]),
     "msa_sparse_attn_prefill": (c_i32, [ctypes.POINTER(MsaBatch), c_i32, c_vp, MsaCache, MsaCache, c_vp, c_vp, c_i32,
-                                        c_f32, c_vp, c_vp, c_vp, c_size, c_vp]),
+                                        c_f32, c_i32, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "msa_sparse_attn_prefill_workspace_size": (c_size, [ctypes.POINTER(MsaBatch), c_i32, c_i32]),
     "msa_lse_merge": (c_i32, [c_i64, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "msa_status_string": (ctypes.c_char_p, [c_i32]),

@@ -50,12 +50,24 @@ constexpr float kLog2eP = 1.4426950408889634f;
 constexpr float kLn2P = 0.6931471805599453f;
 
 struct PrefillWs {
-  int32_t* counts;    // [NB]
-  int32_t* cursor;    // [NB]
-  int32_t* offsets;   // [NB + 1]
-  int32_t* item_off;  // [NB + 1]; item_off[NB] = number of work items
-  int32_t* entries;   // [Nq*Hkv*k] packed t * 64 + j
-  int2* items;        // [max_items] (bucket, chunk)
+  int32_t* counts;      // [NB] rows per (KV head, request, block) bucket, all entries
+  int32_t* cursor;      // [NB]
+  int32_t* rcounts;     // [NB] entries left to the per-block kernel (query-tile path only)
+  int32_t* hcounts;     // [NH] rows per anchor-hash bucket (query-tile path)
+  int32_t* hcursor;     // [NH]
+  int32_t* offsets;     // [NB + 1]
+  int32_t* item_off;    // [NB + 1]; item_off[NB] = number of work items
+  int32_t* entries;     // [Nq*Hkv*k] packed t * 64 + j
+  int2* items;          // [max_items] (bucket, chunk)
+  int32_t* hoffsets;    // [NH + 1]
+  int32_t* row_key;     // [Nq*Hkv] anchor-hash bucket of the row, or -1
+  int32_t* sorted_rows; // [Nq*Hkv] query rows grouped by bucket
+  int2* tiles;          // [max_tiles] (bucket, chunk of rows)
+  int32_t* tile_count;  // [1]
+  uint16_t* dense;      // [NH * 64] each bucket's dense blocks, ascending
+  int32_t* dense_n;     // [NH]
+  uint64_t* cov_mask;   // [Nq*Hkv] slots j whose block is dense in the row's bucket
+  int32_t* row_jt;      // [Nq*Hkv] the row's merged slot, or -1
 };
 
 static size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -76,22 +88,57 @@ static int item_chunk(int64_t total_entries, int G) {
   return c;
 }
 
-size_t prefill_workspace_bytes(int32_t Nq, int32_t Hkv, int32_t k, int32_t B, int32_t max_blocks) {
-  const int64_t NB = (int64_t)Hkv * B * max_blocks;
-  const int64_t E = (int64_t)Nq * Hkv * k;
-  // the work list is sized for the smallest chunk, so it holds the list of any chunk item_chunk picks
-  return a256(NB * 4) * 2 + a256((NB + 1) * 4) * 2 + a256(E * 4) + a256(max_items(E, NB, kMinChunk) * 8);
+int tile_hash_buckets(int max_q);
+size_t tile_dense_bytes(int64_t NH);
+// tiles of >= 16 query rows each, plus one partial tile per non-empty bucket
+static int64_t tile_bound(int64_t rows, int64_t buckets) { return rows / 16 + std::min(rows, buckets) + 1; }
+
+struct PrefillDims {
+  int64_t NB, E, R, NH, NS, max_tiles;
+  int H;
+};
+static PrefillDims prefill_dims(int32_t Nq, int32_t Hkv, int32_t k, int32_t B, int32_t max_blocks, int32_t max_q) {
+  PrefillDims d;
+  d.NB = (int64_t)Hkv * B * max_blocks;
+  d.E = (int64_t)Nq * Hkv * k;
+  d.R = (int64_t)Nq * Hkv;
+  d.NS = (int64_t)Hkv * B;
+  d.H = tile_hash_buckets(max_q);
+  d.NH = d.NS * d.H;
+  d.max_tiles = tile_bound(d.R, d.NH);
+  return d;
 }
 
-static PrefillWs carve(void* ws, int64_t NB, int64_t E) {
+size_t prefill_workspace_bytes(int32_t Nq, int32_t Hkv, int32_t k, int32_t B, int32_t max_blocks, int32_t max_q) {
+  const PrefillDims d = prefill_dims(Nq, Hkv, k, B, max_blocks, max_q);
+  // the work list is sized for the smallest chunk, so it holds the list of any chunk item_chunk picks
+  return a256(d.NB * 4) * 3 + a256(d.NH * 4) * 2 + a256((d.NB + 1) * 4) * 2 + a256(d.E * 4) +
+         a256(max_items(d.E, d.NB, kMinChunk) * 8) + a256((d.NH + 1) * 4) + a256(d.R * 4) * 2 + a256(d.max_tiles * 8) +
+         a256(4) + a256(tile_dense_bytes(d.NH)) + a256(d.NH * 4) + a256(d.R * 8) + a256(d.R * 4);
+}
+
+static PrefillWs carve(void* ws, const PrefillDims& d) {
   char* p = static_cast<char*>(ws);
   PrefillWs w;
-  w.counts = reinterpret_cast<int32_t*>(p); p += a256(NB * 4);
-  w.cursor = reinterpret_cast<int32_t*>(p); p += a256(NB * 4);
-  w.offsets = reinterpret_cast<int32_t*>(p); p += a256((NB + 1) * 4);
-  w.item_off = reinterpret_cast<int32_t*>(p); p += a256((NB + 1) * 4);
-  w.entries = reinterpret_cast<int32_t*>(p); p += a256(E * 4);
-  w.items = reinterpret_cast<int2*>(p);
+  // the counters a launch clears come first and are adjacent: one fill clears them all
+  w.counts = reinterpret_cast<int32_t*>(p); p += a256(d.NB * 4);
+  w.cursor = reinterpret_cast<int32_t*>(p); p += a256(d.NB * 4);
+  w.rcounts = reinterpret_cast<int32_t*>(p); p += a256(d.NB * 4);
+  w.hcounts = reinterpret_cast<int32_t*>(p); p += a256(d.NH * 4);
+  w.hcursor = reinterpret_cast<int32_t*>(p); p += a256(d.NH * 4);
+  w.offsets = reinterpret_cast<int32_t*>(p); p += a256((d.NB + 1) * 4);
+  w.item_off = reinterpret_cast<int32_t*>(p); p += a256((d.NB + 1) * 4);
+  w.entries = reinterpret_cast<int32_t*>(p); p += a256(d.E * 4);
+  w.items = reinterpret_cast<int2*>(p); p += a256(max_items(d.E, d.NB, kMinChunk) * 8);
+  w.hoffsets = reinterpret_cast<int32_t*>(p); p += a256((d.NH + 1) * 4);
+  w.row_key = reinterpret_cast<int32_t*>(p); p += a256(d.R * 4);
+  w.sorted_rows = reinterpret_cast<int32_t*>(p); p += a256(d.R * 4);
+  w.tiles = reinterpret_cast<int2*>(p); p += a256(d.max_tiles * 8);
+  w.tile_count = reinterpret_cast<int32_t*>(p); p += a256(4);
+  w.dense = reinterpret_cast<uint16_t*>(p); p += a256(tile_dense_bytes(d.NH));
+  w.dense_n = reinterpret_cast<int32_t*>(p); p += a256(d.NH * 4);
+  w.cov_mask = reinterpret_cast<uint64_t*>(p); p += a256(d.R * 8);
+  w.row_jt = reinterpret_cast<int32_t*>(p);
   return w;
 }
 
@@ -104,7 +151,8 @@ __global__ void k_fill_i32(int32_t* __restrict__ a, int64_t n, int32_t v) {
 __global__ __launch_bounds__(256) void k_remap_count(int64_t E, int B, int Hkv, int k, int G, int max_blocks,
                                                      const int32_t* __restrict__ cu_q, const int32_t* __restrict__ sel,
                                                      const int32_t* __restrict__ cnt, int32_t* __restrict__ counts,
-                                                     float* __restrict__ part_lse) {
+                                                     float* __restrict__ part_lse,
+                                                     const uint64_t* __restrict__ cov_mask) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= E) return;
   const int64_t tg = idx / k;
@@ -114,7 +162,9 @@ __global__ __launch_bounds__(256) void k_remap_count(int64_t E, int B, int Hkv, 
   if (j < cnt[tg]) {
     const int r = request_of(cu_q, B, t);
     const int b = sel[idx];
-    atomicAdd(&counts[((int64_t)g * B + r) * max_blocks + b], 1);
+    const int64_t bucket = ((int64_t)g * B + r) * max_blocks + b;
+    if (cov_mask && ((cov_mask[tg] >> j) & 1)) return;
+    atomicAdd(&counts[bucket], 1);
   } else {
     for (int h = 0; h < G; ++h) part_lse[idx * G + h] = neg_inf();
   }
@@ -164,7 +214,8 @@ __global__ __launch_bounds__(256) void k_remap_fill(int64_t E, int B, int Hkv, i
                                                     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ sel,
                                                     const int32_t* __restrict__ cnt,
                                                     const int32_t* __restrict__ offsets, int32_t* __restrict__ cursor,
-                                                    int32_t* __restrict__ entries) {
+                                                    int32_t* __restrict__ entries,
+                                                    const uint64_t* __restrict__ cov_mask) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= E) return;
   const int64_t tg = idx / k;
@@ -174,6 +225,7 @@ __global__ __launch_bounds__(256) void k_remap_fill(int64_t E, int B, int Hkv, i
   const int t = (int)(tg / Hkv);
   const int r = request_of(cu_q, B, t);
   const int64_t bucket = ((int64_t)g * B + r) * max_blocks + sel[idx];
+  if (cov_mask && ((cov_mask[tg] >> j) & 1)) return;
   const int slot = offsets[bucket] + atomicAdd(&cursor[bucket], 1);
   entries[slot] = t * 64 + j;
 }
@@ -207,6 +259,9 @@ struct RemapArgs {
   const int32_t* cu_q;
   const int32_t* sel;
   const int32_t* cnt;
+  // when set, entry (t, g, j) with bit j of cov_mask[t*Hkv + g] is left out (the query-tile path
+  // attends to it); the remap then takes the remaining entries only
+  const uint64_t* cov_mask;
 };
 
 // Request of row t: binary search over cu_q[0..B], from the LDS copy when there is one.
@@ -245,6 +300,11 @@ __device__ __forceinline__ void remap_batch(const RemapArgs& a, const int32_t* s
     if (base + 256 * u >= e1) bucket[u] = -2;
     else if (j >= c[u]) bucket[u] = -1;
     else bucket[u] = (g * a.B + remap_request(a, s_cu, t)) * a.max_blocks + sv[u];
+  }
+  if (a.cov_mask) {
+#pragma unroll
+    for (int u = 0; u < kRemapU; ++u)
+      if (bucket[u] >= 0 && ((a.cov_mask[tg[u]] >> (ic[u] - tg[u] * a.k)) & 1)) bucket[u] = -3;
   }
 }
 
@@ -566,40 +626,93 @@ __global__ __launch_bounds__(kThreads, MSA_KVBM_OCC) void k_attn_kvbm(
   }
 }
 
-hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blocks, const int32_t* block_table,
-                               const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const void* q,
-                               const void* kcache, const void* vcache, const int32_t* sel, const int32_t* cnt, int k,
-                               float sm_scale, void* part_o, float* part_lse, void* workspace, hipStream_t stream) {
-  const int64_t NB = (int64_t)Hkv * B * max_blocks;
-  const int64_t E = (int64_t)Nq * Hkv * k;
-  PrefillWs ws = carve(workspace, NB, E);
-  // counts and cursor are adjacent in the workspace: one fill clears both
-  const int64_t n_clear = (int64_t)(ws.offsets - ws.counts);
+bool tile_supported(int G, int D, int max_blocks, int k);
+int tile_tokens(int G);
+hipError_t launch_tile_prep(int64_t rows, int B, int Hkv, int k, int G, int max_blocks, const int32_t* cu_q,
+                            const int32_t* sel, const int32_t* cnt, const int32_t* counts, int cover_min, int H,
+                            int64_t NH, int TT, int32_t* hcounts, int32_t* hcursor, int32_t* row_key,
+                            int32_t* hoffsets, int2* tiles, int32_t* tile_count, int32_t* sorted_rows,
+                            uint16_t* dense, int32_t* dense_n, uint64_t* cov_mask, int32_t* row_jt, float* part_lse,
+                            hipStream_t stream);
+hipError_t launch_attn_tiles(int64_t max_tiles, int B, int Hkv, int G, int D, int k, int max_blocks, int H,
+                             const int32_t* block_table, const int32_t* ctx_len, const int32_t* q_pos, const void* q,
+                             const void* kcache, const void* vcache, const int32_t* sel, const int32_t* hoffsets,
+                             const int32_t* sorted_rows, const uint16_t* dense, const int32_t* dense_n,
+                             const uint64_t* cov_mask, const int32_t* row_jt, const int2* tiles,
+                             const int32_t* tile_count, float scale_log2, void* part_o, float* part_lse,
+                             hipStream_t stream);
+
+hipError_t launch_slot_of(int64_t E, int k, const int32_t* cnt, const uint64_t* cov_mask, const int32_t* row_jt,
+                          int32_t* slot_of, hipStream_t stream);
+
+// Whether msa_sparse_attn_prefill takes the query-tile path for these shapes.
+bool prefill_uses_tiles(int tile_min_rows, int G, int D, int max_blocks, int k) {
+  return tile_min_rows > 0 && tile_supported(G, D, max_blocks, k);
+}
+
+hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blocks, int max_q,
+                               const int32_t* block_table, const int32_t* ctx_len, const int32_t* cu_q,
+                               const int32_t* q_pos, const void* q, const void* kcache, const void* vcache,
+                               const int32_t* sel, const int32_t* cnt, int k, float sm_scale, int tile_min_rows,
+                               void* part_o, float* part_lse, int32_t* slot_of, void* workspace,
+                               hipStream_t stream) {
+  const PrefillDims d = prefill_dims(Nq, Hkv, k, B, max_blocks, max_q);
+  const int64_t NB = d.NB, E = d.E;
+  const bool tiles = prefill_uses_tiles(tile_min_rows, G, D, max_blocks, k) && d.NH < (int64_t(1) << 30);
+  PrefillWs ws = carve(workspace, d);
+  // the counters are adjacent in the workspace: one fill clears them (the tile counters only when used)
+  const int64_t n_clear = (int64_t)((tiles ? ws.offsets : ws.rcounts) - ws.counts);
   const int fill_blocks = (int)((n_clear + 255) / 256 < 4096 ? (n_clear + 255) / 256 : 4096);
   hipLaunchKernelGGL(k_fill_i32, dim3(fill_blocks), dim3(256), 0, stream, ws.counts, n_clear, 0);
   const unsigned eb = (unsigned)((E + 255) / 256);
   const bool lds_remap = NB <= kLdsBuckets;
   const int run = remap_run(E);
   const unsigned rb = (unsigned)((E + run - 1) / run);
-  const RemapArgs ra{E, B, Hkv, k, max_blocks, cu_q, sel, cnt};
-  if (lds_remap)
-    hipLaunchKernelGGL(k_remap_count_lds, dim3(rb), dim3(256), 0, stream, ra, run, G, (int)NB, ws.counts, part_lse);
-  else
-    hipLaunchKernelGGL(k_remap_count, dim3(eb), dim3(256), 0, stream, E, B, Hkv, k, G, max_blocks, cu_q, sel, cnt,
-                       ws.counts, part_lse);
+  const RemapArgs all{E, B, Hkv, k, max_blocks, cu_q, sel, cnt, nullptr};
+  const RemapArgs rest{E, B, Hkv, k, max_blocks, cu_q, sel, cnt, tiles ? ws.cov_mask : nullptr};
+  auto count = [&](const RemapArgs& a, int32_t* target) {
+    if (lds_remap)
+      hipLaunchKernelGGL(k_remap_count_lds, dim3(rb), dim3(256), 0, stream, a, run, G, (int)NB, target, part_lse);
+    else
+      hipLaunchKernelGGL(k_remap_count, dim3(eb), dim3(256), 0, stream, E, B, Hkv, k, G, max_blocks, cu_q, sel, cnt,
+                         target, part_lse, a.cov_mask);
+  };
+  count(all, ws.counts);
+  int32_t* bucket_counts = ws.counts;
+  if (tiles) {
+    // rows into anchor-hash buckets, each bucket's dense blocks, each row's dense slots; then the
+    // entries left to the per-block kernel
+    hipError_t e = launch_tile_prep(d.R, B, Hkv, k, G, max_blocks, cu_q, sel, cnt, ws.counts, tile_min_rows, d.H,
+                                    d.NH, tile_tokens(G), ws.hcounts, ws.hcursor, ws.row_key, ws.hoffsets, ws.tiles,
+                                    ws.tile_count, ws.sorted_rows, ws.dense, ws.dense_n, ws.cov_mask, ws.row_jt,
+                                    part_lse, stream);
+    if (e != hipSuccess) return e;
+    count(rest, ws.rcounts);
+    bucket_counts = ws.rcounts;
+  }
+  if (slot_of) {
+    hipError_t e = launch_slot_of(E, k, cnt, tiles ? ws.cov_mask : nullptr, ws.row_jt, slot_of, stream);
+    if (e != hipSuccess) return e;
+  }
   const int chunk = item_chunk(E, G);
-  hipLaunchKernelGGL(k_remap_scan, dim3(1), dim3(1024), 0, stream, NB, chunk, ws.counts, ws.offsets, ws.item_off,
+  hipLaunchKernelGGL(k_remap_scan, dim3(1), dim3(1024), 0, stream, NB, chunk, bucket_counts, ws.offsets, ws.item_off,
                      ws.items);
   if (lds_remap)
-    hipLaunchKernelGGL(k_remap_fill_lds, dim3(rb), dim3(256), 0, stream, ra, run, (int)NB, ws.offsets, ws.cursor,
+    hipLaunchKernelGGL(k_remap_fill_lds, dim3(rb), dim3(256), 0, stream, rest, run, (int)NB, ws.offsets, ws.cursor,
                        ws.entries);
   else
     hipLaunchKernelGGL(k_remap_fill, dim3(eb), dim3(256), 0, stream, E, B, Hkv, k, max_blocks, cu_q, sel, cnt,
-                       ws.offsets, ws.cursor, ws.entries);
+                       ws.offsets, ws.cursor, ws.entries, rest.cov_mask);
+  const float sl2 = sm_scale * kLog2eP;
+  if (tiles) {
+    hipError_t e = launch_attn_tiles(d.max_tiles, B, Hkv, G, D, k, max_blocks, d.H, block_table, ctx_len, q_pos, q,
+                                     kcache, vcache, sel, ws.hoffsets, ws.sorted_rows, ws.dense, ws.dense_n,
+                                     ws.cov_mask, ws.row_jt, ws.tiles, ws.tile_count, sl2, part_o, part_lse, stream);
+    if (e != hipSuccess) return e;
+  }
   // upper bound on the work items, rounded up to whole XCD rounds
   const int64_t mi = max_items(E, NB, chunk);
   const unsigned grid = (unsigned)(((mi + kXcds - 1) / kXcds) * kXcds);
-  const float sl2 = sm_scale * kLog2eP;
   const bf16* qq = static_cast<const bf16*>(q);
   const bf16* kc = static_cast<const bf16*>(kcache);
   const bf16* vc = static_cast<const bf16*>(vcache);

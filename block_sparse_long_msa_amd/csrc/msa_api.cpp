@@ -44,11 +44,13 @@ hipError_t launch_lse_merge_bf16(int64_t rows, int parts, int G, int D, const vo
                                  void* out, float* lse_out, hipStream_t stream);
 size_t decode_scratch_bytes();
 hipError_t decode_scratch(void** ptr);
-size_t prefill_workspace_bytes(int32_t Nq, int32_t Hkv, int32_t k, int32_t B, int32_t max_blocks);
-hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blocks, const int32_t* block_table,
-                               const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const void* q,
-                               const void* kcache, const void* vcache, const int32_t* sel, const int32_t* cnt, int k,
-                               float sm_scale, void* part_o, float* part_lse, void* workspace, hipStream_t stream);
+size_t prefill_workspace_bytes(int32_t Nq, int32_t Hkv, int32_t k, int32_t B, int32_t max_blocks, int32_t max_q);
+hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blocks, int max_q,
+                               const int32_t* block_table, const int32_t* ctx_len, const int32_t* cu_q,
+                               const int32_t* q_pos, const void* q, const void* kcache, const void* vcache,
+                               const int32_t* sel, const int32_t* cnt, int k, float sm_scale, int tile_min_rows,
+                               void* part_o, float* part_lse, int32_t* slot_of, void* workspace,
+                               hipStream_t stream);
 }  // namespace msa
 
 namespace {
@@ -387,13 +389,14 @@ size_t msa_sparse_attn_prefill_workspace_size(const msa_batch* batch, int32_t nu
   if (!batch || batch->num_queries < 0 || batch->num_requests <= 0 || batch->max_blocks <= 0 || num_kv_heads <= 0 ||
       k <= 0)
     return 0;
-  return msa::prefill_workspace_bytes(batch->num_queries, num_kv_heads, k, batch->num_requests, batch->max_blocks);
+  return msa::prefill_workspace_bytes(batch->num_queries, num_kv_heads, k, batch->num_requests, batch->max_blocks,
+                                      batch->max_q_per_request);
 }
 
 msa_status msa_sparse_attn_prefill(const msa_batch* batch, int32_t G, const void* q, msa_cache k_cache,
                                    msa_cache v_cache, const int32_t* sel, const int32_t* cnt, int32_t k,
-                                   float sm_scale, void* part_o, float* part_lse, void* workspace,
-                                   size_t workspace_bytes, msa_stream_t stream) {
+                                   float sm_scale, int32_t tile_min_rows, void* part_o, float* part_lse,
+                                   int32_t* slot_of, void* workspace, size_t workspace_bytes, msa_stream_t stream) {
   g_last_error.clear();
   if (msa_status s = check_batch(batch)) return s;
   if (msa_status s = check_cache(k_cache, "k_cache")) return s;
@@ -403,13 +406,14 @@ msa_status msa_sparse_attn_prefill(const msa_batch* batch, int32_t G, const void
               MSA_ERR_INVALID_ARG, "k_cache and v_cache shapes differ");
   MSA_REQUIRE(supported_group(G), MSA_ERR_UNSUPPORTED, "G must be 1, 2, 4, 8 or 16, got %d", G);
   MSA_REQUIRE(k >= 1 && k <= kMaxK, MSA_ERR_UNSUPPORTED, "k must be in [1, %d], got %d", kMaxK, k);
+  MSA_REQUIRE(tile_min_rows >= 0, MSA_ERR_INVALID_ARG, "tile_min_rows must be >= 0, got %d", tile_min_rows);
   if (batch->num_queries == 0) return MSA_OK;
   MSA_REQUIRE(q && sel && cnt && part_o && part_lse && workspace, MSA_ERR_INVALID_ARG,
               "q, sel, cnt, part_o, part_lse and workspace must be non-NULL");
   MSA_REQUIRE(aligned16(q) && aligned16(part_o) && aligned16(workspace), MSA_ERR_INVALID_ARG,
               "q, part_o and workspace must be 16-byte aligned");
-  MSA_REQUIRE(aligned4(sel) && aligned4(cnt) && aligned4(part_lse), MSA_ERR_INVALID_ARG,
-              "sel, cnt and part_lse must be 4-byte aligned");
+  MSA_REQUIRE(aligned4(sel) && aligned4(cnt) && aligned4(part_lse) && aligned4(slot_of), MSA_ERR_INVALID_ARG,
+              "sel, cnt, part_lse and slot_of must be 4-byte aligned");
   MSA_REQUIRE((int64_t)batch->num_queries * k_cache.num_heads * k <= 0x7fffffffLL, MSA_ERR_UNSUPPORTED,
               "num_queries*Hkv*k must fit in int32");
   MSA_REQUIRE((int64_t)batch->num_queries < (1LL << 25), MSA_ERR_UNSUPPORTED, "num_queries must be < 2^25");
@@ -419,10 +423,10 @@ msa_status msa_sparse_attn_prefill(const msa_batch* batch, int32_t G, const void
   MSA_REQUIRE(workspace_bytes >= need, MSA_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
               workspace_bytes);
   return from_hip(msa::launch_attn_prefill(batch->num_requests, batch->num_queries, k_cache.num_heads, G,
-                                           k_cache.head_dim, batch->max_blocks, batch->block_table, batch->ctx_len,
-                                           batch->cu_q, batch->q_pos, q, k_cache.data, v_cache.data, sel, cnt, k,
-                                           sm_scale, part_o, part_lse, workspace,
-                                           reinterpret_cast<hipStream_t>(stream)),
+                                           k_cache.head_dim, batch->max_blocks, batch->max_q_per_request,
+                                           batch->block_table, batch->ctx_len, batch->cu_q, batch->q_pos, q,
+                                           k_cache.data, v_cache.data, sel, cnt, k, sm_scale, tile_min_rows, part_o,
+                                           part_lse, slot_of, workspace, reinterpret_cast<hipStream_t>(stream)),
                   "msa_sparse_attn_prefill launch");
 }
 

@@ -90,6 +90,10 @@ class MSAPrefill:
 
     ROW_TILE = 256        # query rows per workgroup of the prefill scorer
     FUSED_MIN_WGS = 256   # half of the two workgroups per CU the scorer runs at
+    # msa_sparse_attn_prefill's query-tile path (tile_min_rows > 0) merges partials on chip; on the long
+    # prefill it cuts the merge from 1.6 to 0.9 ms but its attention is slower than the per-block kernel's,
+    # so by default every selected block keeps its own partial
+    TILE_MIN_ROWS = 0
 
     @classmethod
     def prefers_fused(cls, num_queries: int, Hkv: int) -> bool:
@@ -97,9 +101,10 @@ class MSAPrefill:
         return -(-num_queries // cls.ROW_TILE) * Hkv >= cls.FUSED_MIN_WGS
 
     def __init__(self, batch: Batch, Hkv: int, G: int, D: int, k: int, num_pages: int, device="cuda",
-                 fused=None):
+                 fused=None, tile_min_rows=None):
         Nq, mb = batch.num_queries, batch.max_blocks
         self.batch, self.Hkv, self.G, self.D, self.k, self.num_pages = batch, Hkv, G, D, k, num_pages
+        self.tile_min_rows = self.TILE_MIN_ROWS if tile_min_rows is None else int(tile_min_rows)
         self.fused = self.prefers_fused(Nq, Hkv) if fused is None else bool(fused)
         self.scores = None if self.fused else torch.empty((Nq, Hkv, mb), dtype=torch.float32, device=device)
         self.topk_ws = torch.empty((max(1, msa_index_topk_workspace_size(batch, Hkv, k)),), dtype=torch.uint8,
@@ -125,7 +130,7 @@ class MSAPrefill:
 
     def attend(self, q, kcache, vcache, sm_scale: float, stream=None):
         msa_sparse_attn_prefill(self.batch, self.G, q, kcache, vcache, self.sel, self.cnt, self.k, sm_scale,
-                                self.part_o, self.part_lse, self.ws, stream)
+                                self.part_o, self.part_lse, self.ws, stream, tile_min_rows=self.tile_min_rows)
 
     def merge(self, stream=None):
         rows = self.batch.num_queries * self.Hkv

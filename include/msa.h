@@ -189,23 +189,38 @@ msa_status msa_topk_attn_decode_noalloc(const msa_batch* batch, const float* sco
                                         msa_stream_t stream);
 
 /* KV-block-major prefill attention (section "KV块主序稀疏注意力减少冗余KV移动"; Russian page,
- * third paragraph): the selection is inverted into {(KV head, physical page) -> queries}
- * lists, each selected KV block is staged on chip and attended by every query row that
- * picked it, and each (query row t, KV head g, slot j) gets the partial output of block
- * sel[t,g,j] alone:
+ * third paragraph): the selection is inverted into {(KV head, request, block) -> query rows}
+ * buckets, each selected KV block is staged on chip and attended by the query rows that picked
+ * it, and the partial outputs are combined afterwards by a log-sum-exp reduction (msa_lse_merge).
+ * Causal masking inside a block: key s counts iff s <= q_pos[t] and s < ctx_len[r].
+ *
+ * tile_min_rows = 0: every selected block has its own partial, slot j for block sel[t,g,j]:
  *   part_o[t,g,j,i,:] = softmax_i(scale * q[t, g*G+i] . K_b) V_b   (normalized, bf16)
  *   part_lse[t,g,j,i] = log sum exp of the same logits            (f32; -inf for j >= cnt)
- * Causal masking inside the block: key s counts iff s <= q_pos[t] and s < ctx_len[r].
- *   q       device bf16 [Nq, Hkv*G, D]
+ * tile_min_rows = n >= 1, with G in {4, 8, 16}, k <= 64 and max_blocks <= 16384 (otherwise as 0):
+ * some blocks of a row are attended together and share one slot.  Blocks that at least n query rows
+ * of the request and KV head selected are eligible; rows of the same request and KV head are grouped
+ * by their two eligible blocks with the most rows; a group's dense blocks are the eligible blocks at
+ * least a quarter of its rows (and two or more) selected, at most 64.  Tiles of a group's rows stage
+ * each dense block once for all of their rows that picked it, and every row keeps a running softmax
+ * over the dense blocks it picked.  Then for such a row
+ *   the lowest of their slots holds the softmax over the valid keys of all of them (normalized
+ *   output and LSE, as above), their other slots get part_lse = -inf (part_o not written),
+ * and every other selected block keeps its own slot as with 0.  The grouping depends on sel and cnt
+ * only, so results are deterministic; the merged output of msa_lse_merge is the same attention
+ * either way, up to rounding.
+ *   q        device bf16 [Nq, Hkv*G, D]
  *   k_cache, v_cache  [pages, 128, Hkv, D]
  *   sel, cnt  from msa_topk_blocks
- *   part_o  device bf16 [Nq, Hkv, k, G, D];  part_lse  device f32 [Nq, Hkv, k, G]
+ *   part_o   device bf16 [Nq, Hkv, k, G, D];  part_lse  device f32 [Nq, Hkv, k, G]
+ *   slot_of  device i32 [Nq, Hkv, k] or NULL: for j < cnt[t,g], the slot that holds block sel[t,g,j]'s
+ *            share (slot s holds the softmax over the blocks with slot_of = s); -1 for j >= cnt
  *   workspace  device, >= msa_sparse_attn_prefill_workspace_size(...) bytes
  * Combine the partials with msa_lse_merge(rows = Nq*Hkv, parts = k, ...). */
 msa_status msa_sparse_attn_prefill(const msa_batch* batch, int32_t G, const void* q, msa_cache k_cache,
                                    msa_cache v_cache, const int32_t* sel, const int32_t* cnt, int32_t k,
-                                   float sm_scale, void* part_o, float* part_lse, void* workspace,
-                                   size_t workspace_bytes, msa_stream_t stream);
+                                   float sm_scale, int32_t tile_min_rows, void* part_o, float* part_lse,
+                                   int32_t* slot_of, void* workspace, size_t workspace_bytes, msa_stream_t stream);
 /* Workspace bytes for msa_sparse_attn_prefill on this batch (0 for invalid arguments). */
 size_t msa_sparse_attn_prefill_workspace_size(const msa_batch* batch, int32_t num_kv_heads, int32_t k);
 

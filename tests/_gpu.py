@@ -136,15 +136,16 @@ class DeviceView:
         return (v.float() if v.is_floating_point() else v).cpu().numpy()
 
 
-def prefill(dev, b, sel, cnt, k=None):
-    """KV-block-major attention partials, then the LSE merge."""
+def prefill(dev, b, sel, cnt, k=None, tile_min=0, slot_of=None):
+    """KV-block-major attention partials (tile_min_rows = tile_min), then the LSE merge."""
     wl = dev.wl
     k = k or wl.k
     msa = lib()
     po = torch.full((wl.Nq, wl.Hkv, k, wl.G, wl.D), float("nan"), dtype=torch.bfloat16, device="cuda")
     pl = nan_f32(wl.Nq, wl.Hkv, k, wl.G)
     ws = torch.empty(msa.msa_sparse_attn_prefill_workspace_size(b, wl.Hkv, k), dtype=torch.uint8, device="cuda")
-    msa.msa_sparse_attn_prefill(b, wl.G, dev.q, dev.kcache, dev.vcache, sel, cnt, k, dev.scale, po, pl, ws)
+    msa.msa_sparse_attn_prefill(b, wl.G, dev.q, dev.kcache, dev.vcache, sel, cnt, k, dev.scale, po, pl, ws,
+                                tile_min_rows=tile_min, slot_of=slot_of)
     out = torch.full((wl.Nq, wl.Hq, wl.D), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse = nan_f32(wl.Nq, wl.Hq)
     msa.msa_lse_merge(wl.Nq * wl.Hkv, k, wl.G, wl.D, po, pl, out, lse)

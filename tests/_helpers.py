@@ -6,6 +6,8 @@ import types
 import numpy as np
 import torch
 
+import oracle
+
 
 def np_inputs(inp) -> types.SimpleNamespace:
     """NumPy views of an ``msa_inputs.Inputs`` (bf16 upcast exactly to float32)."""
@@ -49,3 +51,64 @@ def selection_excused(sel_a, cnt_a, sel_b, cnt_b, scores_ref, k, tol=1e-3):
                     f"row {t} group {g}: block {blk} differs with score {s[blk]} vs k-th {kth}")
             diff.append((t, g))
     return diff
+
+
+def block_rows(sel, cnt, q_req):
+    """Number of query rows of each (request, KV head) that selected each block: {(r, g, b): rows}."""
+    rows = {}
+    Nq, Hkv, _ = sel.shape
+    for t in range(Nq):
+        for g in range(Hkv):
+            for j in range(int(cnt[t, g])):
+                key = (int(q_req[t]), g, int(sel[t, g, j]))
+                rows[key] = rows.get(key, 0) + 1
+    return rows
+
+
+def check_slot_of(slot_of, sel, cnt, q_req, n_min):
+    """slot_of as the prefill attention's header states it: -1 past cnt; every selected slot maps to the
+    lowest slot of its group, which maps to itself; only blocks that at least n_min rows of the request
+    and KV head selected share a slot with others (n_min = 0: every slot is its own).  Returns
+    {(t, g): {slot: [member slots]}}."""
+    Nq, Hkv, k = sel.shape
+    rows = block_rows(sel, cnt, q_req)
+    groups = {}
+    for t in range(Nq):
+        for g in range(Hkv):
+            c = int(cnt[t, g])
+            assert np.all(slot_of[t, g, c:] == -1), f"row {t} head {g}: slot_of past cnt"
+            grp = {}
+            for j in range(c):
+                s = int(slot_of[t, g, j])
+                assert 0 <= s <= j, f"row {t} head {g}: slot {j} maps to {s}"
+                grp.setdefault(s, []).append(j)
+            for s, members in grp.items():
+                assert members[0] == s, f"row {t} head {g}: group {members} not held by its lowest slot"
+                if len(members) > 1 or n_min <= 0:
+                    assert n_min > 0 or members == [s]
+                    for j in members:
+                        assert rows[(int(q_req[t]), g, int(sel[t, g, j]))] >= n_min, "ineligible block merged"
+            groups[(t, g)] = grp
+    return groups
+
+
+def expected_partials(x, sel, cnt, groups):
+    """Per-slot partials the prefill attention must write for the given slot groups: the oracle's softmax
+    over the valid keys of every block of a group in the group's slot, lse = -inf in the group's other
+    slots (and past cnt)."""
+    ref_po, ref_pl = oracle.block_partials(x.q, x.kcache, x.vcache, x.block_table, x.ctx_len, x.q_req, x.q_pos,
+                                           sel, cnt, x.wl.block, x.scale)
+    G = x.wl.G
+    for (t, g), grp in groups.items():
+        r, p = int(x.q_req[t]), int(x.q_pos[t])
+        for s, members in grp.items():
+            if len(members) == 1:
+                continue
+            blocks = np.asarray([sel[t, g, j] for j in members])
+            K, V = oracle.selected_kv(x.kcache, x.vcache, x.block_table[r], blocks, len(blocks), g, p,
+                                      int(x.ctx_len[r]), x.wl.block)
+            for i in range(G):
+                ref_po[t, g, s, i], ref_pl[t, g, s, i] = oracle.attend(x.q[t, g * G + i], K, V, x.scale)
+            for j in members[1:]:
+                ref_pl[t, g, j, :] = -np.inf
+    return ref_po, ref_pl

@@ -169,12 +169,14 @@ def test_topk_attn_decode_noalloc_rejects_batches_beyond_its_scratch(lib):
 def test_prefill_attention_rejects(lib):
     b = _batch(Nq=40, maxq=40)
     kc, vc = _cache(), _cache()
-    assert lib.msa_sparse_attn_prefill(ctypes.byref(b), 3, FAKE, kc, vc, FAKE, FAKE, 4, 0.1, FAKE, FAKE, FAKE,
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(b), 3, FAKE, kc, vc, FAKE, FAKE, 4, 0.1, 0, FAKE, FAKE, None, FAKE,
                                        1 << 30, None) == UNSUPPORTED
-    assert lib.msa_sparse_attn_prefill(ctypes.byref(b), 4, FAKE, kc, _cache(D=128), FAKE, FAKE, 4, 0.1, FAKE, FAKE,
-                                       FAKE, 1 << 30, None) == INVALID
-    assert lib.msa_sparse_attn_prefill(ctypes.byref(b), 4, FAKE, kc, vc, FAKE, FAKE, 4, 0.1, FAKE, FAKE, FAKE, 16,
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(b), 4, FAKE, kc, _cache(D=128), FAKE, FAKE, 4, 0.1, 0, FAKE, FAKE,
+                                       None, FAKE, 1 << 30, None) == INVALID
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(b), 4, FAKE, kc, vc, FAKE, FAKE, 4, 0.1, 0, FAKE, FAKE, None, FAKE, 16,
                                        None) == WS_SMALL
+    assert lib.msa_sparse_attn_prefill(ctypes.byref(b), 4, FAKE, kc, vc, FAKE, FAKE, 4, 0.1, -1, FAKE, FAKE, None, FAKE,
+                                       1 << 30, None) == INVALID
 
 
 @no_gpu

@@ -10,8 +10,8 @@ import pytest
 
 import msa_inputs as mi
 import oracle
-from _gpu import announce, batch, decode_attention, host, prefill, scores, setup, topk, topk_page_table
-from _helpers import assert_attn_close, np_inputs, selection_excused
+from _gpu import announce, batch, decode_attention, host, poison_i32, prefill, scores, setup, topk, topk_page_table
+from _helpers import assert_attn_close, check_slot_of, expected_partials, np_inputs, selection_excused
 
 pytestmark = pytest.mark.gpu
 
@@ -83,6 +83,55 @@ def _check_against_oracle(dev, cpu):
                                            sel, cnt, wl.block, x.scale)
     assert_attn_close(out, ref_o, what="merged output")
     assert np.abs(lse - ref_l).max() <= 1e-3
+
+
+TILE_CASES = ["tiny_prefill_2k", "ragged_multi_request", "chunk_over_prefix", "g16_d64", "k64_g16", "many_requests",
+              "remap_many_buckets", "g2_k_over_candidates"]
+
+
+@pytest.mark.parametrize("n_min", [0, 1, 3, 40])
+@pytest.mark.parametrize("name", TILE_CASES)
+def test_tile_path_matches_oracle(name, n_min):
+    """tile_min_rows = n_min: slot_of groups each row's selected slots (only blocks that n_min rows or more
+    selected share a slot); every slot holds the oracle's softmax over exactly its group's blocks, the other
+    slots of a group lse = -inf; the merged output is the oracle's attention over the selection."""
+    announce("prefill tiles", name, f"n_min={n_min}")
+    dev, cpu = setup(_wl(name))
+    x = np_inputs(cpu)
+    wl = dev.wl
+    b = batch(dev)
+    s = scores(dev, b)
+    sel, cnt = topk(dev, b, s)
+    slot_of = poison_i32(wl.Nq, wl.Hkv, wl.k)
+    po, pl, out, lse = [host(t) for t in prefill(dev, b, sel, cnt, tile_min=n_min, slot_of=slot_of)]
+    sel, cnt, slot_of = host(sel), host(cnt), host(slot_of)
+    groups = check_slot_of(slot_of, sel, cnt, x.q_req, n_min)
+    merged = sum(len(m) > 1 for grp in groups.values() for m in grp.values())
+    if n_min in (1, 3) and name in ("tiny_prefill_2k", "chunk_over_prefix", "ragged_multi_request"):
+        assert merged > 0, "the tile path merged nothing"
+    ref_po, ref_pl = expected_partials(x, sel, cnt, groups)
+    present = ~np.isneginf(ref_pl[..., 0])                                 # [Nq, Hkv, k]
+    assert np.all(np.isneginf(pl[~present])), "absent and merged-away slots must carry lse = -inf"
+    assert_attn_close(po[present], ref_po[present], what="partials")
+    assert np.abs(pl[present] - ref_pl[present]).max() <= 1e-3
+    ref_o, ref_l = oracle.sparse_attention(x.q, x.kcache, x.vcache, x.block_table, x.ctx_len, x.q_req, x.q_pos,
+                                           sel, cnt, wl.block, x.scale)
+    assert_attn_close(out, ref_o, what="merged output")
+    assert np.abs(lse - ref_l).max() <= 1e-3
+
+
+def test_tile_path_is_deterministic():
+    """Rows are placed in tiles with atomics; results must not depend on that placement."""
+    announce("prefill tiles determinism")
+    dev, _ = setup(_wl("chunk_over_prefix", seed=8))
+    b = batch(dev)
+    sel, cnt = topk(dev, b, scores(dev, b))
+    a = [host(t) for t in prefill(dev, b, sel, cnt, tile_min=2)]
+    for _ in range(3):
+        c = [host(t) for t in prefill(dev, b, sel, cnt, tile_min=2)]
+        for u, v in zip(a, c):
+            fin = ~np.isnan(u)
+            assert np.array_equal(u[fin].view(np.uint8), v[fin].view(np.uint8))
 
 
 def test_prefill_is_deterministic():
