@@ -13,8 +13,9 @@
 //   as 16 contiguous bytes, whose 8 values become the A operand of 8 MFMAs (output row m of
 //   MFMA c is d = 8m + c).  No LDS transpose, no shuffles, every V row read as whole
 //   64-byte segments.  The four waves' (max, sum, O) are combined through LDS.  A row is split
-//   over several workgroups only as far as needed to occupy the chip; the splits are then
-//   combined by k_merge_splits.
+//   over several workgroups only as far as needed to occupy the chip; the last split of a row to
+//   finish combines the row's split partials (merge_row), so there is no second launch, or, for
+//   rows split more than kFusedMergeMax ways, k_merge_splits does.
 // k_select_attend: the top-k, the page table and k_attn_decode in one launch -- each attention
 //   workgroup selects its own row's blocks from the scores (row_topk, topk_select.h) and takes the
 //   chosen pages' ids from LDS instead of a page table in memory.
@@ -129,7 +130,97 @@ struct DecodeLds {
   static constexpr int OST = D + 4;  // padded row of the per-wave outputs
   float m[4][16], l[4][16];
   __align__(16) float o[4][16][OST];
+  unsigned ticket;  // this split's place among the row's splits to finish
 };
+
+// Split partials are written by one workgroup and read by another, which may run on another XCD
+// with its own L2.  They are stored and loaded as agent-scope relaxed atomics (global stores and
+// loads with sc1 set), which are coherent across the XCDs by themselves, so the hand-off needs no
+// device-scope fence: such a fence writes back and invalidates the whole L2 of every XCD.
+__device__ __forceinline__ void store_agent(float* p, f32x4 v) {
+  uint64_t* d = reinterpret_cast<uint64_t*>(p);
+  const uint64_t lo = ((uint64_t)__float_as_uint(v[1]) << 32) | __float_as_uint(v[0]);
+  const uint64_t hi = ((uint64_t)__float_as_uint(v[3]) << 32) | __float_as_uint(v[2]);
+  __hip_atomic_store(d, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(d + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 load_agent4(const float* p) {
+  const uint64_t* s = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t lo = __hip_atomic_load(s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(s + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const f32x4 v = {__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                   __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
+  return v;
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The last split of row rho to finish folds the row's nsplit partials (O_j normalized, LSE_j) into
+// the output: LSE = M + ln sum_j exp(LSE_j - M) with M = max_j LSE_j, O = sum_j exp(LSE_j - LSE) O_j
+// (section "KV块主序稀疏注意力减少冗余KV移动").  Thread e takes the 4-float chunk e of the G x D
+// output and reads the parts in batches of eight, all loads of a batch issued together.  A part with
+// LSE = -inf (a split past the row's last page) has weight 0 and its O is not read.
+template <int D>
+__device__ __forceinline__ void merge_row(int G, int rho, int nsplit, const float* __restrict__ ws_o,
+                                          const float* __restrict__ ws_lse, bf16* __restrict__ out,
+                                          float* __restrict__ lse_out) {
+  constexpr int kBatch = 8;
+  for (int e = threadIdx.x; e < G * D / 4; e += 256) {
+    const int h = (4 * e) / D, d = (4 * e) % D;
+    const float* pl = ws_lse + (int64_t)rho * nsplit * G + h;
+    const float* po = ws_o + ((int64_t)rho * nsplit * G + h) * D + d;
+    float m = neg_inf(), sum = 0.f;
+    f32x4 o = fzero4();
+    for (int j0 = 0; j0 < nsplit; j0 += kBatch) {
+      float x[kBatch];
+      f32x4 v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) x[i] = j0 + i < nsplit ? load_agent(pl + (int64_t)(j0 + i) * G) : neg_inf();
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        v[i] = x[i] != neg_inf() ? load_agent4(po + (int64_t)(j0 + i) * G * D) : fzero4();
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (x[i] == neg_inf()) continue;
+        const float mn = fmaxf(m, x[i]);
+        const float a = (m == neg_inf()) ? 0.f : __expf(m - mn);
+        const float wj = __expf(x[i] - mn);
+        sum = sum * a + wj;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o[t] = o[t] * a + wj * v[i][t];
+        m = mn;
+      }
+    }
+    const float inv = 1.f / sum;
+    uint2 pk;
+    pk.x = pack_bf2(o[0] * inv, o[1] * inv);
+    pk.y = pack_bf2(o[2] * inv, o[3] * inv);
+    *reinterpret_cast<uint2*>(out + ((int64_t)rho * G + h) * D + d) = pk;
+    if (d == 0 && lse_out) lse_out[(int64_t)rho * G + h] = m + __logf(sum);
+  }
+}
+
+// Split hand-off: every thread's partial stores are complete (vmcnt(0)) before the workgroup takes
+// its ticket from the row's arrival counter; the split that draws nsplit - 1 is the last, returns the
+// counter to zero for the next call and merges the row.
+template <int D>
+__device__ __forceinline__ void finish_split(DecodeLds<D>& sm, int G, int rho, int nsplit,
+                                             uint32_t* __restrict__ counters, const float* __restrict__ ws_o,
+                                             const float* __restrict__ ws_lse, bf16* __restrict__ out,
+                                             float* __restrict__ lse_out) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    sm.ticket = __hip_atomic_fetch_add(counters + rho, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (sm.ticket != (unsigned)(nsplit - 1)) return;
+  if (threadIdx.x == 0) __hip_atomic_store(counters + rho, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  merge_row<D>(G, rho, nsplit, ws_o, ws_lse, out, lse_out);
+}
 
 // Page ids of a run read from the row's page table in memory; the first two arrive with the row
 // length, so the first K/V loads wait for one round trip, not two.
@@ -146,14 +237,16 @@ struct PagesInLds {
 
 // Workgroup (split sp, row rho) attends to the row's pages [sp*ppw, (sp+1)*ppw) with two pages of
 // loads in flight (one being consumed, the next arriving).  With nsplit = 1 it writes the final
-// bf16 output and LSE; otherwise an fp32 partial and its LSE per (row, split) for the merge.
+// bf16 output and LSE; otherwise an fp32 partial and its LSE per (row, split), which the row's last
+// split to finish merges.
 template <int D, typename Pages>
 __device__ __forceinline__ void attend_run(DecodeLds<D>& sm, int G, const bf16* __restrict__ q,
                                            const bf16* __restrict__ kview, const bf16* __restrict__ vview,
                                            int64_t page_stride, int64_t token_stride, const Pages& pages, int len,
                                            int rho, int sp, int ppw, int nsplit, float scale_log2,
                                            bf16* __restrict__ out, float* __restrict__ lse_out,
-                                           float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+                                           float* __restrict__ ws_o, float* __restrict__ ws_lse,
+                                           uint32_t* __restrict__ counters) {
   constexpr int KW = D / 32;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, qd = lane >> 4;
   const int j0 = sp * ppw;
@@ -161,7 +254,8 @@ __device__ __forceinline__ void attend_run(DecodeLds<D>& sm, int G, const bf16* 
   const int j1 = min(j0 + ppw, npages);
   const int64_t part = (int64_t)rho * nsplit + sp;
   if (j0 >= j1) {  // only with nsplit > 1: a split past the row's last page
-    if (tid < G) ws_lse[part * G + tid] = neg_inf();
+    if (tid < G) store_agent(ws_lse + part * G + tid, neg_inf());
+    if (counters) finish_split<D>(sm, G, rho, nsplit, counters, ws_o, ws_lse, out, lse_out);
     return;
   }
   // Page j of the run; a prefetch past the run's end re-reads one token of its last page (valid
@@ -238,10 +332,11 @@ __device__ __forceinline__ void attend_run(DecodeLds<D>& sm, int G, const bf16* 
       if (d == 0 && lse_out) lse_out[(int64_t)rho * G + h] = lse;
     } else {
       f32x4 r = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-      *reinterpret_cast<f32x4*>(ws_o + (part * G + h) * D + d) = r;
-      if (d == 0) ws_lse[part * G + h] = lse;
+      store_agent(ws_o + (part * G + h) * D + d, r);
+      if (d == 0) store_agent(ws_lse + part * G + h, lse);
     }
   }
+  if (nsplit > 1 && counters) finish_split<D>(sm, G, rho, nsplit, counters, ws_o, ws_lse, out, lse_out);
 }
 
 // Decode attention over a page table in memory: workgroup (split, row) = blockIdx.x as (rho*nsplit + sp).
@@ -250,7 +345,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
     int G, const bf16* __restrict__ q, const bf16* __restrict__ kview, const bf16* __restrict__ vview,
     int64_t page_stride, int64_t token_stride, const int32_t* __restrict__ page_table, int k,
     const int32_t* __restrict__ row_len, float scale_log2, int ppw, int nsplit, bf16* __restrict__ out,
-    float* __restrict__ lse_out, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+    float* __restrict__ lse_out, float* __restrict__ ws_o, float* __restrict__ ws_lse,
+    uint32_t* __restrict__ counters) {
   __shared__ DecodeLds<D> sm;
   const int sp = (int)(blockIdx.x % (unsigned)nsplit), rho = (int)(blockIdx.x / (unsigned)nsplit);
   const int j0 = sp * ppw;
@@ -262,7 +358,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
   asm volatile("" ::"s"(pt0), "s"(pt1), "s"(len));  // issue the three loads here, side by side
   const PagesInMemory pages{pt, j0, pt0, pt1};
   attend_run<D>(sm, G, q, kview, vview, page_stride, token_stride, pages, len, rho, sp, ppw, nsplit, scale_log2,
-                out, lse_out, ws_o, ws_lse);
+                out, lse_out, ws_o, ws_lse, counters);
 }
 
 // Top-k, page table and decode attention in one launch.  Workgroup (split sp, row rho) selects its
@@ -281,7 +377,8 @@ __global__ __launch_bounds__(256, 2) void k_select_attend(
     int32_t* __restrict__ sel, int32_t* __restrict__ cnt, int32_t* __restrict__ page_table,
     int32_t* __restrict__ row_len, int G, const bf16* __restrict__ q, const bf16* __restrict__ kcache,
     const bf16* __restrict__ vcache, float scale_log2, int ppw, int nsplit, bf16* __restrict__ out,
-    float* __restrict__ lse_out, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+    float* __restrict__ lse_out, float* __restrict__ ws_o, float* __restrict__ ws_lse,
+    uint32_t* __restrict__ counters) {
   constexpr int NW = 4, NT = 256;
   __shared__ DecodeLds<D> sm;
   __shared__ RowTopkLds<NW> sh;
@@ -326,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void k_select_attend(
   __syncthreads();
   const PagesInLds pages{s_pt};
   attend_run<D>(sm, G, q, kcache, vcache, D, (int64_t)Hkv * D, pages, s_len, rho, sp, ppw, nsplit, scale_log2, out,
-                lse_out, ws_o, ws_lse);
+                lse_out, ws_o, ws_lse, counters);
 }
 
 // Merge of the decode splits: one workgroup per (row, head).  Thread (g, c) folds the parts
@@ -485,6 +582,14 @@ __global__ __launch_bounds__(256) void k_lse_merge(int64_t rows, int parts, int 
   if (lse_out && lane < G) lse_out[row * G + lane] = s_lse[wv][lane];
 }
 
+#ifndef MSA_DECODE_FUSED_MERGE_MAX
+#define MSA_DECODE_FUSED_MERGE_MAX 8
+#endif
+// Rows split at most this many ways are merged by their last split inside the attention launch (one
+// batch of part loads per thread); more splits take the separate merge kernel, which spreads a row's
+// merge over G workgroups instead of looping over the parts in one.
+constexpr int kFusedMergeMax = MSA_DECODE_FUSED_MERGE_MAX;
+
 int decode_splits(int rows, int k) {
   int nsplit = std::min(k, std::max(1, (MSA_DECODE_TARGET_WGS + rows - 1) / rows));
   const int ppw = (k + nsplit - 1) / nsplit;
@@ -504,9 +609,10 @@ static hipError_t launch_merge_splits(int rows, int G, int D, int nsplit, const 
 hipError_t launch_attn_decode(int rows, int G, int D, const void* q, const void* kview, const void* vview,
                               int64_t page_stride, int64_t token_stride, const int32_t* page_table, int k,
                               const int32_t* row_len, float sm_scale, void* out, float* lse, float* ws_o,
-                              float* ws_lse, hipStream_t stream) {
+                              float* ws_lse, uint32_t* counters, hipStream_t stream) {
   const int nsplit = decode_splits(rows, k);
   const int ppw = (k + nsplit - 1) / nsplit;
+  const bool fused = nsplit <= kFusedMergeMax;
   dim3 grid((unsigned)((int64_t)nsplit * rows)), block(256);
   const float sl2 = sm_scale * kLog2e;
   const bf16* qq = static_cast<const bf16*>(q);
@@ -515,12 +621,12 @@ hipError_t launch_attn_decode(int rows, int G, int D, const void* q, const void*
   bf16* oo = static_cast<bf16*>(out);
   if (D == 128)
     hipLaunchKernelGGL(k_attn_decode<128>, grid, block, 0, stream, G, qq, kk, vv, page_stride, token_stride,
-                       page_table, k, row_len, sl2, ppw, nsplit, oo, lse, ws_o, ws_lse);
+                       page_table, k, row_len, sl2, ppw, nsplit, oo, lse, ws_o, ws_lse, fused ? counters : nullptr);
   else
     hipLaunchKernelGGL(k_attn_decode<64>, grid, block, 0, stream, G, qq, kk, vv, page_stride, token_stride,
-                       page_table, k, row_len, sl2, ppw, nsplit, oo, lse, ws_o, ws_lse);
+                       page_table, k, row_len, sl2, ppw, nsplit, oo, lse, ws_o, ws_lse, fused ? counters : nullptr);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nsplit == 1) return e;
+  if (e != hipSuccess || nsplit == 1 || fused) return e;
   return launch_merge_splits(rows, G, D, nsplit, ws_o, ws_lse, oo, lse, stream);
 }
 
@@ -528,16 +634,17 @@ hipError_t launch_attn_decode(int rows, int G, int D, const void* q, const void*
 // separate top-k kernel (measured on million-token rows), so those rows keep the two launches.
 int select_attend_max_blocks() { return 256 * 16; }
 
-// Top-k + page table + decode attention in one launch (plus the split merge); max_blocks must be
+// Top-k + page table + decode attention (split merge included) in one launch; max_blocks must be
 // at most select_attend_max_blocks().  Same splits, pages and arithmetic as the separate calls.
 hipError_t launch_select_attend(int B, int Nq, int Hkv, int max_blocks, const int32_t* block_table,
                                 const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const float* scores,
                                 int k, int32_t* sel, int32_t* cnt, int32_t* page_table, int32_t* row_len, int G, int D,
                                 const void* q, const void* kcache, const void* vcache, float sm_scale, void* out,
-                                float* lse, float* ws_o, float* ws_lse, hipStream_t stream) {
+                                float* lse, float* ws_o, float* ws_lse, uint32_t* counters, hipStream_t stream) {
   const int rows = Nq * Hkv;
   const int nsplit = decode_splits(rows, k);
   const int ppw = (k + nsplit - 1) / nsplit;
+  const bool fused = nsplit <= kFusedMergeMax;
   const dim3 grid((unsigned)((int64_t)nsplit * rows)), block(256);
   const float sl2 = sm_scale * kLog2e;
   const bf16* qq = static_cast<const bf16*>(q);
@@ -546,7 +653,8 @@ hipError_t launch_select_attend(int B, int Nq, int Hkv, int max_blocks, const in
   bf16* oo = static_cast<bf16*>(out);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, stream, B, Hkv, max_blocks, block_table, ctx_len, cu_q, q_pos, scores, k,
-                       sel, cnt, page_table, row_len, G, qq, kc, vc, sl2, ppw, nsplit, oo, lse, ws_o, ws_lse);
+                       sel, cnt, page_table, row_len, G, qq, kc, vc, sl2, ppw, nsplit, oo, lse, ws_o, ws_lse,
+                       fused ? counters : nullptr);
   };
   const int r = max_blocks <= 256 ? 1 : max_blocks <= 512 ? 2 : max_blocks <= 1024 ? 4 : max_blocks <= 2048 ? 8 : 16;
   if (D == 128) {
@@ -563,14 +671,15 @@ hipError_t launch_select_attend(int B, int Nq, int Hkv, int max_blocks, const in
     else go(k_select_attend<64, 16>);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nsplit == 1) return e;
+  if (e != hipSuccess || nsplit == 1 || fused) return e;
   return launch_merge_splits(rows, G, D, nsplit, ws_o, ws_lse, oo, lse, stream);
 }
 
-// Split partials of msa_topk_attn_decode_noalloc, for callers that cannot allocate device memory.
-// One copy of this array lives on every GPU the library runs on, for the life of the process.  Every
-// split writes its own LSE (-inf for a split past its row's last page) before the merge reads it, and
-// an absent split is read from split 0 with weight 0, so nothing has to be cleared between calls.
+// Split partials and row arrival counters of msa_topk_attn_decode_noalloc, for callers that cannot
+// allocate device memory.  One copy of this array lives on every GPU the library runs on, for the life
+// of the process.  It starts zeroed (static storage), every call returns the counters it used to zero,
+// and every split writes its own LSE (-inf for a split past its row's last page) before the merge
+// reads it, so nothing has to be cleared between calls.
 constexpr size_t kDecodeScratchBytes = MSA_DECODE_NOALLOC_SCRATCH_BYTES;
 static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
 constexpr int kMaxDevices = 64;

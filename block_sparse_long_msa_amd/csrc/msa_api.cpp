@@ -35,11 +35,11 @@ hipError_t launch_select_attend(int B, int Nq, int Hkv, int max_blocks, const in
                                 const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const float* scores,
                                 int k, int32_t* sel, int32_t* cnt, int32_t* page_table, int32_t* row_len, int G, int D,
                                 const void* q, const void* kcache, const void* vcache, float sm_scale, void* out,
-                                float* lse, float* ws_o, float* ws_lse, hipStream_t stream);
+                                float* lse, float* ws_o, float* ws_lse, uint32_t* counters, hipStream_t stream);
 hipError_t launch_attn_decode(int rows, int G, int D, const void* q, const void* kview, const void* vview,
                               int64_t page_stride, int64_t token_stride, const int32_t* page_table, int k,
                               const int32_t* row_len, float sm_scale, void* out, float* lse, float* ws_o,
-                              float* ws_lse, hipStream_t stream);
+                              float* ws_lse, uint32_t* counters, hipStream_t stream);
 hipError_t launch_lse_merge_bf16(int64_t rows, int parts, int G, int D, const void* part_o, const float* part_lse,
                                  void* out, float* lse_out, hipStream_t stream);
 size_t decode_scratch_bytes();
@@ -264,8 +264,35 @@ size_t msa_sparse_attn_decode_workspace_size(int32_t rows, int32_t G, int32_t D,
   const int nsplit = msa::decode_splits(rows, k);
   if (nsplit == 1) return 0;  // each row in one workgroup: outputs are written directly
   const size_t parts = (size_t)rows * nsplit * G;
-  return align256(parts * D * sizeof(float)) + align256(parts * sizeof(float));
+  return align256((size_t)rows * sizeof(uint32_t)) + align256(parts * D * sizeof(float)) +
+         align256(parts * sizeof(float));
 }
+
+namespace {
+
+// Split workspace of the decode attention: partial O and partial LSE from the start of the buffer, one
+// arrival counter per row at its end (the last 256-byte-aligned rows * 4 bytes below the buffer's
+// 256-byte-aligned size).  Calls with fewer rows use a tail of the same counter region and no call's
+// partials reach it, so counters that start at zero stay valid from call to call for one buffer and
+// size; each call returns the counters it used to zero.
+struct DecodeSplitWs {
+  uint32_t* counters = nullptr;
+  float* o = nullptr;
+  float* lse = nullptr;
+};
+DecodeSplitWs decode_split_ws(void* workspace, size_t workspace_bytes, int rows, int G, int D, int k) {
+  DecodeSplitWs w;
+  if (msa_sparse_attn_decode_workspace_size(rows, G, D, k) == 0) return w;
+  const size_t parts = (size_t)rows * msa::decode_splits(rows, k) * G;
+  char* base = static_cast<char*>(workspace);
+  w.o = reinterpret_cast<float*>(base);
+  w.lse = reinterpret_cast<float*>(base + align256(parts * D * sizeof(float)));
+  const size_t end = workspace_bytes & ~(size_t)255;
+  w.counters = reinterpret_cast<uint32_t*>(base + end - align256((size_t)rows * sizeof(uint32_t)));
+  return w;
+}
+
+}  // namespace
 
 msa_status msa_sparse_attn_decode(int32_t rows, int32_t G, int32_t D, const void* q, const void* k_base,
                                   const void* v_base, int64_t page_stride, int64_t token_stride,
@@ -291,13 +318,10 @@ msa_status msa_sparse_attn_decode(int32_t rows, int32_t G, int32_t D, const void
   const size_t need = msa_sparse_attn_decode_workspace_size(rows, G, D, k);
   MSA_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), MSA_ERR_WORKSPACE_TOO_SMALL,
               "workspace needs %zu bytes, got %zu", need, workspace_bytes);
-  const size_t parts = (size_t)rows * msa::decode_splits(rows, k) * G;
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_lse = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(parts * D * sizeof(float)))
-                       : nullptr;
+  const DecodeSplitWs ws = decode_split_ws(workspace, workspace_bytes, rows, G, D, k);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return from_hip(msa::launch_attn_decode(rows, G, D, q, k_base, v_base, page_stride, token_stride, page_table, k,
-                                          row_len, sm_scale, out, lse, ws_o, ws_lse, st),
+                                          row_len, sm_scale, out, lse, ws.o, ws.lse, ws.counters, st),
                   "msa_sparse_attn_decode launch");
 }
 
@@ -346,16 +370,14 @@ msa_status topk_attn_decode(const msa_batch* batch, const float* scores, int32_t
     MSA_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), MSA_ERR_WORKSPACE_TOO_SMALL,
                 "workspace needs %zu bytes, got %zu", need, workspace_bytes);
   }
-  const size_t parts = (size_t)rows * msa::decode_splits(rows, k) * G;
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_lse = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(parts * D * sizeof(float)))
-                       : nullptr;
+  const DecodeSplitWs ws =
+      decode_split_ws(workspace, use_scratch ? msa::decode_scratch_bytes() : workspace_bytes, rows, G, D, k);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (batch->max_blocks <= msa::select_attend_max_blocks())
     return from_hip(msa::launch_select_attend(batch->num_requests, batch->num_queries, Hkv, batch->max_blocks,
                                               batch->block_table, batch->ctx_len, batch->cu_q, batch->q_pos, scores,
                                               k, sel, cnt, page_table, row_len, G, D, q, k_cache.data, v_cache.data,
-                                              sm_scale, out, lse, ws_o, ws_lse, st),
+                                              sm_scale, out, lse, ws.o, ws.lse, ws.counters, st),
                     "msa_topk_attn_decode launch");
   // rows too long to select inside the attention workgroup: the two launches of the separate calls
   hipError_t e = msa::launch_topk_page_table(batch->num_requests, batch->num_queries, Hkv, batch->max_blocks,
@@ -363,7 +385,7 @@ msa_status topk_attn_decode(const msa_batch* batch, const float* scores, int32_t
                                              sel, cnt, page_table, row_len, st);
   if (e != hipSuccess) return from_hip(e, "msa_topk_attn_decode top-k launch");
   return from_hip(msa::launch_attn_decode(rows, G, D, q, k_cache.data, v_cache.data, D, (int64_t)Hkv * D, page_table,
-                                          k, row_len, sm_scale, out, lse, ws_o, ws_lse, st),
+                                          k, row_len, sm_scale, out, lse, ws.o, ws.lse, ws.counters, st),
                   "msa_topk_attn_decode attention launch");
 }
 

@@ -44,7 +44,8 @@ class MSADecode:
         self.row_len = torch.empty((self.rows,), dtype=torch.int32, device=device)
         self.out = torch.empty((Nq, Hkv * G, D), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((Nq, Hkv * G), dtype=torch.float32, device=device)
-        self.ws = torch.empty((msa_sparse_attn_decode_workspace_size(self.rows, G, D, k),), dtype=torch.uint8,
+        # zeroed once: the split merge's row arrival counters at its end start at zero
+        self.ws = torch.zeros((msa_sparse_attn_decode_workspace_size(self.rows, G, D, k),), dtype=torch.uint8,
                               device=device)
 
     def score(self, q_idx, kidx, stream=None):
@@ -165,7 +166,7 @@ class MSAPrefillQueryMajor:
         self.out = torch.empty((Nq, Hkv * G, D), dtype=torch.bfloat16, device=device)
         self.lse = torch.empty((Nq, Hkv * G), dtype=torch.float32, device=device)
         ws = msa_sparse_attn_decode_workspace_size(self.rows, G, D, k)
-        self.ws = torch.empty((ws,), dtype=torch.uint8, device=device) if ws else None
+        self.ws = torch.zeros((ws,), dtype=torch.uint8, device=device) if ws else None
 
     def score(self, q_idx, kidx, stream=None):
         msa_index_score(self.batch, q_idx, kidx, self.scores, stream)

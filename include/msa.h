@@ -138,16 +138,21 @@ msa_status msa_topk_page_table(const msa_batch* batch, int32_t num_kv_heads, int
  * Token i of row rho is virtual page v = page_table[rho, i/128], slot s = i%128, and its
  * element d is at k_base[v*page_stride + s*token_stride + d] (same for v_base).
  * Softmax scale sm_scale, natural-log LSE.  When there are too few rows to fill the GPU, each
- * row's pages are split over several workgroups and the parts combined by a log-sum-exp merge
- * through the workspace; otherwise no workspace is used (size 0, pointer may be NULL).
+ * row's pages are split over several workgroups and the last of them to finish combines the parts
+ * by a log-sum-exp merge through the workspace; otherwise no workspace is used (size 0, pointer may
+ * be NULL).  The workspace ends in one arrival counter per row (its last 256-byte-aligned 4*rows
+ * bytes): zero the whole workspace once before its first use and pass the same workspace_bytes
+ * with it on every call; each call returns the counters to zero.
  * Only a row's last page may be partial, which holds for selections in ascending block order, so
  * the same call also runs prefill rows query-major (rows = Nq*Hkv, one query token per row,
  * page table from msa_topk_page_table): each row reads its own k blocks, with no partials.
  *   q        device bf16 [rows*G, D]  (= [Nq, Hq, D] when rows = Nq*Hkv)
  *   out      device bf16 [rows*G, D]
  *   lse      device f32 [rows*G] or NULL
- *   workspace  device, >= msa_sparse_attn_decode_workspace_size(rows, G, D, k) bytes
- * Rows with row_len = 0 are invalid input; rows*k must fit in int32. */
+ *   workspace  device, >= msa_sparse_attn_decode_workspace_size(rows, G, D, k) bytes, zeroed before
+ *              its first use (above)
+ * Rows with row_len = 0 are invalid input; rows*k must fit in int32.  Calls that share a workspace
+ * must not overlap in time. */
 msa_status msa_sparse_attn_decode(int32_t rows, int32_t G, int32_t D, const void* q, const void* k_base,
                                   const void* v_base, int64_t page_stride, int64_t token_stride,
                                   const int32_t* page_table, int32_t k, const int32_t* row_len,
@@ -156,7 +161,7 @@ msa_status msa_sparse_attn_decode(int32_t rows, int32_t G, int32_t D, const void
 size_t msa_sparse_attn_decode_workspace_size(int32_t rows, int32_t G, int32_t D, int32_t k);
 
 /* msa_topk_page_table followed by msa_sparse_attn_decode on the caches' per-KV-head strided views,
- * in one launch (plus the split merge).  Each attention workgroup selects its row's blocks itself,
+ * in one launch (the split merge included).  Each attention workgroup selects its row's blocks itself,
  * so the page table never makes a round trip through memory before attention starts; the pages name
  * handing the top-k to decode attention on chip as open work for MSA's small kernels (Chinese page,
  * section "遗留问题"; Japanese page, "今後の取り組み").  Outputs and results are identical to the
@@ -166,7 +171,8 @@ size_t msa_sparse_attn_decode_workspace_size(int32_t rows, int32_t G, int32_t D,
  *   scores            device f32 [Nq, Hkv, max_blocks] as written by msa_index_score
  *   k_cache, v_cache  [pages, 128, Hkv, D]
  *   q                 device bf16 [Nq, Hkv*G, D];  out  device bf16 [Nq, Hkv*G, D];  lse  f32 [Nq, Hkv*G] or NULL
- *   workspace         device, >= msa_sparse_attn_decode_workspace_size(Nq*Hkv, G, D, k) bytes */
+ *   workspace         device, >= msa_sparse_attn_decode_workspace_size(Nq*Hkv, G, D, k) bytes, zeroed
+ *                     before its first use, as for msa_sparse_attn_decode */
 msa_status msa_topk_attn_decode(const msa_batch* batch, const float* scores, int32_t k, msa_cache k_cache,
                                 msa_cache v_cache, int32_t G, const void* q, float sm_scale, int32_t* sel,
                                 int32_t* cnt, int32_t* page_table, int32_t* row_len, void* out, float* lse,
@@ -175,8 +181,9 @@ msa_status msa_topk_attn_decode(const msa_batch* batch, const float* scores, int
 /* msa_topk_attn_decode for callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc.  Same arguments, outputs and results as
  * msa_topk_attn_decode, with no workspace: when rows have to be split over several workgroups, the split
- * partials go to a static array of MSA_DECODE_NOALLOC_SCRATCH_BYTES bytes that the library holds on each
- * GPU it runs on until the process ends.  This call allocates nothing (no hipMalloc, no library
+ * partials and the row arrival counters go to a static array of MSA_DECODE_NOALLOC_SCRATCH_BYTES bytes
+ * (zero when the library is loaded) that the library holds on each GPU it runs on until the process
+ * ends.  This call allocates nothing (no hipMalloc, no library
  * allocation).  A batch whose split partials need more than that (msa_sparse_attn_decode_workspace_size
  * of Nq*Hkv rows above the limit: at most 16 query heads per KV head, D = 128 and close to 256 rows)
  * returns MSA_ERR_UNSUPPORTED and launches nothing.  Every call on one GPU shares that GPU's array:

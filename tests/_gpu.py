@@ -89,7 +89,7 @@ def decode_attention(dev, pt, rl, k=None):
     rows = wl.Nq * wl.Hkv
     out = torch.full((wl.Nq, wl.Hq, wl.D), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse = nan_f32(wl.Nq, wl.Hq)
-    ws = torch.empty(msa.msa_sparse_attn_decode_workspace_size(rows, wl.G, wl.D, k), dtype=torch.uint8,
+    ws = torch.zeros(msa.msa_sparse_attn_decode_workspace_size(rows, wl.G, wl.D, k), dtype=torch.uint8,
                      device="cuda")
     msa.msa_sparse_attn_decode(rows, wl.G, wl.D, dev.q, dev.kcache, dev.vcache, wl.D, wl.Hkv * wl.D, pt, k, rl,
                                dev.scale, out, lse, ws)
@@ -107,7 +107,7 @@ def topk_attn_decode(dev, b, s, k=None):
     pt, rl = poison_i32(rows, k), poison_i32(rows)
     out = torch.full((wl.Nq, wl.Hq, wl.D), float("nan"), dtype=torch.bfloat16, device="cuda")
     lse = nan_f32(wl.Nq, wl.Hq)
-    ws = torch.empty(msa.msa_sparse_attn_decode_workspace_size(rows, wl.G, wl.D, k), dtype=torch.uint8,
+    ws = torch.zeros(msa.msa_sparse_attn_decode_workspace_size(rows, wl.G, wl.D, k), dtype=torch.uint8,
                      device="cuda")
     msa.msa_topk_attn_decode(b, s, k, dev.kcache, dev.vcache, wl.G, dev.q, dev.scale, sel, cnt, pt, rl, out, lse, ws)
     return sel, cnt, pt, rl, out, lse

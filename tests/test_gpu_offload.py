@@ -37,7 +37,7 @@ def test_decode_with_kv_on_host(ctx, nq, Hq, Hkv, D, k):
     out_h = torch.full_like(out_d, float("nan"))
     lse_h = torch.full_like(lse_d, float("nan"))
     ws_n = msa.msa_sparse_attn_decode_workspace_size(rows, wl.G, wl.D, wl.k)
-    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda") if ws_n else None
+    ws = torch.zeros(ws_n, dtype=torch.uint8, device="cuda") if ws_n else None
     msa.msa_sparse_attn_decode(rows, wl.G, wl.D, dev.q, kh, vh, wl.D, wl.Hkv * wl.D, pt, wl.k, rl, dev.scale,
                                out_h, lse_h, ws)
     torch.cuda.synchronize()
