@@ -302,8 +302,8 @@ def measure(args, name, batch):
         attn_bytes = sel_tok * wl.D * 2 * 2                      # K and V rows of the selected tokens
         if fused_decode:                                         # + the scores the fused top-k reads, once
             attn_bytes += wl.Nq * wl.Hkv * wl.max_blocks * 4
-        kname = ("msa_topk_attn_decode (top-k, page table, attention)" if fused_decode else "k_attn_decode") + \
-            "+k_merge_splits"
+        kname = ("msa_topk_attn_decode (top-k, page table, attention" if fused_decode else "k_attn_decode (attention") + \
+            ", split merge)"
         roof_attn = {"kernel": kname, "bound": "host link" if kv_on_host else "hbm",
                      "achieved": attn_bytes / (attend_ms * 1e-3) / 1e9,
                      "peak": HOST_LINK_PEAK_GBS if kv_on_host else HBM_PEAK_GBS, "unit": "GB/s",
