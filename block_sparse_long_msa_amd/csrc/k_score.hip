@@ -13,7 +13,7 @@
 //      blocks of one request through a double-buffered LDS stage with fully coalesced loads.
 //    - k_score_decode (larger rows): one workgroup per (request, block), loading straight from
 //      HBM into MFMA operand registers (every 16-lane group reads whole 64-byte segments).
-//  * k_score_prefill: one workgroup per (256 query rows, KV head).  A GEMM over the causal
+//  * k_score_prefill: one workgroup per (512 or 256 query rows, KV head).  A GEMM over the causal
 //    range, staging each key-index block in LDS once for 256 queries whose index vectors
 //    stay in registers, with the per-block max fused into the epilogue so that token-level
 //    scores never reach memory.  With TOPK > 0 the same kernel keeps each row's top-k on chip
@@ -292,7 +292,11 @@ __global__ __launch_bounds__(256, 2) void k_score_decode_lds(
   }
 }
 
-constexpr int kPrefTQ = 256;  // query rows per workgroup (64 per wave)
+// Waves per workgroup of the prefill scorer, 64 query rows each: 8 (one workgroup per CU, each staged
+// block serving 512 rows) when the launch has a workgroup for every CU, else 4 (256 rows, two
+// workgroups per CU), so that short prompts still spread over the chip.
+constexpr int kPrefWideW = 8, kPrefNarrowW = 4;
+constexpr int kPrefWideMinWgs = 256;
 constexpr int kPrefSB = 16;   // blocks buffered per score flush
 constexpr int kPrefTargetWgs = 512;  // a split score launch aims for two workgroups per CU
 constexpr int kFusedTopK = 16;  // largest k the fused scorer + top-k keeps per row
@@ -349,19 +353,22 @@ __device__ __forceinline__ void bitonic_sort_desc(uint64_t (&v)[N]) {
 // nsplit > 1 (TOPK == 0 only): the blocks a row tile needs are cut into nsplit contiguous runs, one
 // workgroup per run, so that small problems still fill the chip.  A block's scores do not depend on
 // the run that computes them; the first run also writes the -inf tail.
-template <int DI, int TOPK>
-__global__ __launch_bounds__(256, 2) void k_score_prefill(
+template <int DI, int TOPK, int W>
+__global__ __launch_bounds__(64 * W, 8 / W) void k_score_prefill(
     int B, int Nq, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ ctx_len,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q_idx,
     const bf16* __restrict__ kidx, int Hkv, float* __restrict__ scores, int k, int32_t* __restrict__ sel,
     int32_t* __restrict__ cnt, int nsplit) {
+  constexpr int kPrefThreads = 64 * W;
+  constexpr int kPrefTQ = kPrefThreads;  // query rows per workgroup (64 per wave, one per thread)
   constexpr int KW = DI / 32;
   constexpr int BLKE = kBlock * DI;  // elements of one staged key-index block
   constexpr int CPR = DI / 8;        // 16-byte chunks per token row
-  constexpr int kLoadsPerWave = kBlock * CPR / 64 / 4;  // 64-chunk loads per wave per block
+  constexpr int kLoadsPerWave = kBlock * CPR / 64 / W;  // 64-chunk loads per wave per block
   // Two buffers (the next block arrives while the current one is multiplied) of unpadded token rows
-  // in 16-byte chunks, swizzled by kidx_slot, plus the score buffer: 80 KiB at DI = 128, so two
-  // workgroups share a CU.  The score buffer's first words also carry the position reduction.
+  // in 16-byte chunks, swizzled by kidx_slot, plus the score buffer: 96 KiB at DI = 128 with eight
+  // waves (one workgroup per CU), 80 KiB with four (two per CU).  The score buffer's first words also
+  // carry the position reduction.
   __shared__ __attribute__((aligned(16))) bf16 ks[2][BLKE];
   __shared__ float sbuf[kPrefTQ][kPrefSB];
   int* wred = reinterpret_cast<int*>(&sbuf[0][0]);
@@ -375,6 +382,11 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int last_row = min(row0 + kPrefTQ, Nq) - 1;
   const int r_first = request_of(cu_q, B, row0), r_last = request_of(cu_q, B, last_row);
+  // Eight waves: waves w and w + 4 share a SIMD.  The first of each pair issues first whenever both are
+  // ready, so the pair drifts out of step and one's MFMA bursts overlap the other's operand reads and
+  // maxima instead of both waiting on the same LDS reads (measured: 3-5% on the long prefill; with
+  // four waves per workgroup the two waves of a SIMD belong to different workgroups and it lost).
+  if (W == 8 && w < 4) __builtin_amdgcn_s_setprio(1);
 
   for (int r = r_first; r <= r_last; ++r) {
     const int qa = max(row0, cu_q[r]), qb = min(row0 + kPrefTQ, cu_q[r + 1]);
@@ -401,10 +413,15 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
       pmin = min(pmin, __shfl_xor(pmin, m, kWave));
     }
     __syncthreads();  // the previous request's flush has read sbuf, which wred overlays
-    if (lane == 0) { wred[w] = pmax; wred[4 + w] = pmin; }
+    if (lane == 0) { wred[w] = pmax; wred[W + w] = pmin; }
     __syncthreads();
-    pmax = max(max(wred[0], wred[1]), max(wred[2], wred[3]));
-    pmin = min(min(wred[4], wred[5]), min(wred[6], wred[7]));
+    pmax = wred[0];
+    pmin = wred[W];
+#pragma unroll
+    for (int i = 1; i < W; ++i) {
+      pmax = max(pmax, wred[i]);
+      pmin = min(pmin, wred[W + i]);
+    }
     const int nb = pmax / kBlock + 1;  // blocks needed by at least one row
 
     // fused top-k state (TOPK > 0) of local row tid: its last candidate block and its best keys
@@ -432,7 +449,7 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
       const bf16* kb = kidx + ((int64_t)page * kBlock * Hkv + g) * DI;
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i) {
-        const int grp = 4 * i + w;                         // wave-uniform group of 64 chunks
+        const int grp = W * i + w;                         // wave-uniform group of 64 chunks
         const int row = grp * (64 / CPR) + lane / CPR, p = lane % CPR;
         const bf16* src = kb + (int64_t)row * Hkv * DI + 8 * (p ^ kidx_slot<DI>(row));
         const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)(&ks[buf][grp * 64 * 8]);
@@ -509,8 +526,8 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
       __syncthreads();
       if constexpr (TOPK == 0) {
         // flush: 16 consecutive threads write 16 consecutive blocks of one row
-        for (int it = 0; it < kPrefTQ / 16; ++it) {
-          const int lrow = it * 16 + (tid >> 4), bb = tid & 15, row = row0 + lrow, b = b0 + bb;
+        for (int it = 0; it < kPrefTQ / (kPrefThreads / 16); ++it) {
+          const int lrow = it * (kPrefThreads / 16) + (tid >> 4), bb = tid & 15, row = row0 + lrow, b = b0 + bb;
           if (row >= qa && row < qb && b < b1) scores[((int64_t)row * Hkv + g) * max_blocks + b] = sbuf[lrow][bb];
         }
       } else {
@@ -531,7 +548,7 @@ __global__ __launch_bounds__(256, 2) void k_score_prefill(
     if constexpr (TOPK == 0) {
       // non-candidate tail, written by the first run
       const int tail = split == 0 ? max_blocks - nb : 0;
-      for (int e = tid; e < (qb - qa) * tail; e += 256) {
+      for (int e = tid; e < (qb - qa) * tail; e += kPrefThreads) {
         const int row = qa + e / tail, b = nb + e % tail;
         scores[((int64_t)row * Hkv + g) * max_blocks + b] = neg_inf();
       }
@@ -584,23 +601,47 @@ hipError_t launch_score_decode(int B, int Di, const int32_t* block_table, int ma
   return hipGetLastError();
 }
 
+namespace {
+
+// Workgroup shape and row tiles of a prefill scorer launch: eight waves when the 512-row tiles give
+// every CU a workgroup, else four.
+struct PrefillShape {
+  int waves, tiles;
+};
+PrefillShape prefill_shape(int Nq, int Hkv) {
+  const int wide = (Nq + 64 * kPrefWideW - 1) / (64 * kPrefWideW);
+  if ((int64_t)wide * Hkv >= kPrefWideMinWgs) return {kPrefWideW, wide};
+  return {kPrefNarrowW, (Nq + 64 * kPrefNarrowW - 1) / (64 * kPrefNarrowW)};
+}
+
+template <int TOPK, int W, typename... Args>
+void launch_prefill(int Di, dim3 grid, hipStream_t stream, Args... args) {
+  if (Di == 128)
+    hipLaunchKernelGGL((k_score_prefill<128, TOPK, W>), grid, dim3(64 * W), 0, stream, args...);
+  else
+    hipLaunchKernelGGL((k_score_prefill<64, TOPK, W>), grid, dim3(64 * W), 0, stream, args...);
+}
+
+}  // namespace
+
 hipError_t launch_score_prefill(int B, int Nq, int Di, const int32_t* block_table, int max_blocks,
                                 const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const void* q_idx,
                                 const void* kidx, int Hkv, float* scores, hipStream_t stream) {
-  const int tiles = (Nq + kPrefTQ - 1) / kPrefTQ;
+  const PrefillShape sh = prefill_shape(Nq, Hkv);
   // Few row tiles (short prompts): cut each tile's blocks into runs, doubling the runs while the
   // launch stays within kPrefTargetWgs workgroups and there are blocks for every run.
   int nsplit = 1;
-  while ((int64_t)tiles * Hkv * nsplit * 2 <= kPrefTargetWgs && nsplit * 2 <= max_blocks) nsplit *= 2;
-  dim3 grid(tiles * Hkv * nsplit), block(256);
+  while ((int64_t)sh.tiles * Hkv * nsplit * 2 <= kPrefTargetWgs && nsplit * 2 <= max_blocks) nsplit *= 2;
+  const dim3 grid(sh.tiles * Hkv * nsplit);
   const bf16* qi = static_cast<const bf16*>(q_idx);
   const bf16* ki = static_cast<const bf16*>(kidx);
-  if (Di == 128)
-    hipLaunchKernelGGL((k_score_prefill<128, 0>), grid, block, 0, stream, B, Nq, block_table, max_blocks, ctx_len,
-                       cu_q, q_pos, qi, ki, Hkv, scores, 0, nullptr, nullptr, nsplit);
+  int32_t* none = nullptr;
+  if (sh.waves == kPrefWideW)
+    launch_prefill<0, kPrefWideW>(Di, grid, stream, B, Nq, block_table, max_blocks, ctx_len, cu_q, q_pos, qi, ki, Hkv,
+                                  scores, 0, none, none, nsplit);
   else
-    hipLaunchKernelGGL((k_score_prefill<64, 0>), grid, block, 0, stream, B, Nq, block_table, max_blocks, ctx_len,
-                       cu_q, q_pos, qi, ki, Hkv, scores, 0, nullptr, nullptr, nsplit);
+    launch_prefill<0, kPrefNarrowW>(Di, grid, stream, B, Nq, block_table, max_blocks, ctx_len, cu_q, q_pos, qi, ki,
+                                    Hkv, scores, 0, none, none, nsplit);
   return hipGetLastError();
 }
 
@@ -610,16 +651,17 @@ hipError_t launch_score_topk_prefill(int B, int Nq, int Di, const int32_t* block
                                      const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos,
                                      const void* q_idx, const void* kidx, int Hkv, int k, int32_t* sel, int32_t* cnt,
                                      hipStream_t stream) {
-  const int tiles = (Nq + kPrefTQ - 1) / kPrefTQ;
-  dim3 grid(tiles * Hkv), block(256);
+  const PrefillShape sh = prefill_shape(Nq, Hkv);
+  const dim3 grid(sh.tiles * Hkv);
   const bf16* qi = static_cast<const bf16*>(q_idx);
   const bf16* ki = static_cast<const bf16*>(kidx);
-  if (Di == 128)
-    hipLaunchKernelGGL((k_score_prefill<128, kFusedTopK>), grid, block, 0, stream, B, Nq, block_table, max_blocks,
-                       ctx_len, cu_q, q_pos, qi, ki, Hkv, nullptr, k, sel, cnt, 1);
+  float* none = nullptr;
+  if (sh.waves == kPrefWideW)
+    launch_prefill<kFusedTopK, kPrefWideW>(Di, grid, stream, B, Nq, block_table, max_blocks, ctx_len, cu_q, q_pos,
+                                           qi, ki, Hkv, none, k, sel, cnt, 1);
   else
-    hipLaunchKernelGGL((k_score_prefill<64, kFusedTopK>), grid, block, 0, stream, B, Nq, block_table, max_blocks,
-                       ctx_len, cu_q, q_pos, qi, ki, Hkv, nullptr, k, sel, cnt, 1);
+    launch_prefill<kFusedTopK, kPrefNarrowW>(Di, grid, stream, B, Nq, block_table, max_blocks, ctx_len, cu_q, q_pos,
+                                             qi, ki, Hkv, none, k, sel, cnt, 1);
   return hipGetLastError();
 }
 

@@ -86,11 +86,12 @@ class MSAPrefill:
     never reach memory and ``scores`` is not kept; on the long-prefill workload this is faster than
     the two calls.  ``fused=False`` runs msa_index_score then msa_topk_blocks and keeps the scores.
     ``fused=None`` (the default) takes the fused call when its launch fills the chip, i.e. has at
-    least ``FUSED_MIN_WGS`` workgroups (one per 256 query rows and KV head); shorter chunks take the
+    least ``FUSED_MIN_WGS`` workgroups of 256 query rows per KV head; shorter chunks take the
     two calls, whose scorer splits each row tile's blocks over several workgroups."""
 
-    ROW_TILE = 256        # query rows per workgroup of the prefill scorer
-    FUSED_MIN_WGS = 256   # half of the two workgroups per CU the scorer runs at
+    ROW_TILE = 256        # query rows per four-wave workgroup of the prefill scorer
+    FUSED_MIN_WGS = 256   # half of the two four-wave workgroups per CU (the scorer takes eight-wave
+                          # workgroups of 512 rows, one per CU, from 512 such workgroups on)
     # msa_sparse_attn_prefill's query-tile path (tile_min_rows > 0) merges partials on chip; on the long
     # prefill it cuts the merge from 1.6 to 0.9 ms but its attention is slower than the per-block kernel's,
     # so by default every selected block keeps its own partial

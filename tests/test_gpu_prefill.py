@@ -10,7 +10,7 @@ import pytest
 
 import msa_inputs as mi
 import oracle
-from _gpu import announce, batch, decode_attention, host, poison_i32, prefill, scores, setup, topk, topk_page_table
+from _gpu import announce, batch, decode_attention, host, lib, poison_i32, prefill, scores, setup, topk, topk_page_table
 from _helpers import assert_attn_close, check_slot_of, expected_partials, np_inputs, selection_excused
 
 pytestmark = pytest.mark.gpu
@@ -162,3 +162,56 @@ def test_query_major_matches_oracle(name):
                                            sel, cnt, wl.block, x.scale)
     assert_attn_close(out, ref_o, what="query-major output")
     assert np.abs(lse - ref_l).max() <= 1e-3
+
+
+WIDE_CASES = {
+    # 4 row tiles of 512 x 64 KV heads = 256 workgroups: the scorer takes eight-wave workgroups
+    "wide_hkv64_d64": dict(ctx=[2048], nq=[2048], Hq=64, Hkv=64, D=64, Di=64, k=4),
+    # three requests in 9 tiles of 512 rows x 32 KV heads, tiles straddling request boundaries, Di = 128
+    "wide_ragged_di128": dict(ctx=[3000, 1200, 5000], nq=[1500, 700, 1900], Hq=32, Hkv=32, D=64, Di=128, k=6),
+}
+
+
+def _sample_rows(cu_q, Nq, tile=512, step=37):
+    """Rows the oracle checks one by one: every step-th row, both ends of every request and of every
+    512-row tile."""
+    rows = set(range(0, Nq, step))
+    for c in cu_q:
+        rows.update(x for x in (c - 1, c) if 0 <= x < Nq)
+    for t0 in range(0, Nq, tile):
+        rows.update(x for x in (t0 - 1, t0, t0 + 1) if 0 <= x < Nq)
+    return np.asarray(sorted(rows))
+
+
+@pytest.mark.parametrize("name", list(WIDE_CASES))
+def test_wide_scorer_workgroups_match_oracle(name):
+    """Launches big enough for the eight-wave scorer (one workgroup of 512 rows per CU): block scores
+    of sampled rows against the oracle, the fused top-k bit for bit against the oracle's top-k of the
+    GPU's own scores, and the two calls' selection identical to the fused one."""
+    announce("prefill wide scorer", name)
+    c = dict(WIDE_CASES[name])
+    ctx, nq = c.pop("ctx"), c.pop("nq")
+    dev, cpu = setup(mi.small_workload(ctx, nq, seed=57, **c))
+    wl = dev.wl
+    x = np_inputs(cpu)
+    b = batch(dev)
+    s_dev = scores(dev, b)
+    s = host(s_dev)
+    sel2, cnt2 = topk(dev, b, s_dev)
+    msa = lib()
+    self_sel, self_cnt = poison_i32(wl.Nq, wl.Hkv, wl.k), poison_i32(wl.Nq, wl.Hkv)
+    nws = msa.msa_index_topk_workspace_size(b, wl.Hkv, wl.k)
+    assert nws == 0, "k <= 16 runs the fused kernel"
+    msa.msa_index_topk(b, dev.q_idx, dev.kidx, wl.k, self_sel, self_cnt, None)
+    fsel, fcnt = host(self_sel), host(self_cnt)
+    assert np.array_equal(fsel, host(sel2)) and np.array_equal(fcnt, host(cnt2)), "fused and two-call top-k differ"
+
+    rows = _sample_rows(x.cu_q, wl.Nq)
+    ref = oracle.index_scores(x.q_idx[rows], x.kidx, x.block_table, x.ctx_len, x.q_req[rows], x.q_pos[rows], wl.block)
+    got = s[rows]
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), "candidate masks differ"
+    fin = np.isfinite(ref)
+    assert np.abs(got[fin] - ref[fin]).max() <= 1e-2
+    o_sel, o_cnt = oracle.topk_blocks(got.astype(np.float64), x.q_pos[rows], wl.block, wl.k)
+    assert np.array_equal(fsel[rows], o_sel) and np.array_equal(fcnt[rows], o_cnt), \
+        "fused top-k differs from the oracle's on the GPU's scores"
