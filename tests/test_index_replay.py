@@ -210,6 +210,8 @@ CASES = [  # (context lengths, query counts, Hkv, G, D, k)
     ([900, 520], [400, 130], 2, 16, 64, 3),
     ([640], [640], 4, 1, 128, 2),
     ([300 + 37 * i for i in range(12)], [1 + (i % 7) * 9 for i in range(12)], 4, 4, 128, 3),
+    # more (KV head, request, block) buckets than one LDS histogram holds (the global-atomic remap)
+    ([100000, 90000, 50000], [10, 5, 20], 8, 2, 64, 8),
 ]
 
 
@@ -227,3 +229,65 @@ def test_tile_and_residual_indices_in_range(case, n_min):
     x = random_batch(np.random.default_rng(200 + case), ctx, nq, Hkv, k)
     covered = replay_tiles(x, Hkv, G, D, k, n_min)
     replay_kvbm(x, Hkv, G, D, k, covered)
+
+
+def test_long_prefill_shape_vectorized():
+    """The long prefill's shape (32,768 rows over a 98,304-token prefix, 8 KV heads of 8 query heads,
+    D = 128, top-16), on a random valid selection: the remap's buckets, offsets and work items, and for
+    every entry the Q, output-slot, LSE and K/V element indices the per-block kernel forms, checked in
+    int64 against their arrays (vectorized; the per-workgroup walk above is too slow at this size)."""
+    rng = np.random.default_rng(300)
+    Nq, prefix, Hkv, G, D, k = 32768, 98304, 8, 8, 128, 16
+    L = prefix + Nq
+    mb = L // BLOCK
+    pos = np.arange(prefix, L)
+    ncand = pos // BLOCK + 1
+    # k distinct blocks per (row, KV head) among the row's candidates, ascending
+    sel = np.empty((Nq, Hkv, k), dtype=np.int64)
+    for g in range(Hkv):
+        keys = rng.random((Nq, mb), dtype=np.float32)
+        keys[np.arange(mb)[None, :] >= ncand[:, None]] = 2.0          # never among the k smallest
+        sel[:, g, :] = np.sort(np.argpartition(keys, k, axis=1)[:, :k], axis=1)
+    assert np.all(sel < ncand[:, None, None])
+    bt = rng.permutation(mb)                                          # one request's pages
+    P = mb
+    E = Nq * Hkv * k
+    t = np.repeat(np.arange(Nq), Hkv * k)
+    g = np.tile(np.repeat(np.arange(Hkv), k), Nq)
+    j = np.tile(np.arange(k), Nq * Hkv)
+    b = sel.reshape(-1)
+    NB = Hkv * 1 * mb
+    bucket = g * mb + b
+    assert bucket.min() >= 0 and bucket.max() < NB
+    counts = np.bincount(bucket, minlength=NB)
+    chunk = item_chunk(E, G)
+    assert chunk <= K_CHUNK
+    nitems = -(-counts // chunk)
+    assert nitems.sum() <= max_items(E, NB, chunk)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    assert offsets[-1] == E and E < 2 ** 31, "entry indices fit in int32"
+    code = t * 64 + j
+    assert code.max() < 2 ** 31 and np.array_equal(code >> 6, t) and np.array_equal(code & 63, j)
+    # per entry: Q of each of the G heads, output slot, partial and LSE elements, staged K/V rows
+    Hq = Hkv * G
+    for h in (0, G - 1):
+        q_elem = (t * Hq + g * G + h) * D
+        assert q_elem.min() >= 0 and q_elem.max() + D <= Nq * Hq * D
+        orow = ((t * Hkv + g) * k + j) * G + h
+        assert orow.min() >= 0 and orow.max() < Nq * Hkv * k * G
+        assert orow.max() * D + D <= Nq * Hkv * k * G * D                 # part_o, indexed in int64
+        assert orow.max() * D >= 2 ** 31, "this shape needs 64-bit partial offsets"
+    page = bt[b]
+    in_block = np.minimum(BLOCK, L - b * BLOCK)
+    assert in_block.min() >= 1
+    last_tok = np.minimum(BLOCK - 1, in_block - 1)
+    kv_elem = (page * BLOCK * Hkv + g) * D + last_tok * Hkv * D
+    assert kv_elem.min() >= 0 and kv_elem.max() + D <= P * BLOCK * Hkv * D
+    # work items: every item's entries inside its bucket, at most one chunk of them
+    item_bucket = np.repeat(np.arange(NB), nitems)
+    first = np.concatenate([[0], np.cumsum(nitems)])[:-1]
+    item_chunk_idx = np.arange(nitems.sum()) - np.repeat(first, nitems)
+    e_begin = offsets[item_bucket] + item_chunk_idx * chunk
+    e_end = np.minimum(e_begin + chunk, offsets[item_bucket + 1])
+    assert np.all(e_end > e_begin) and np.all(e_end - e_begin <= K_CHUNK)
+    assert (e_end - e_begin).sum() == E
