@@ -252,7 +252,7 @@ def measure(args, name, batch):
             if stage == "score":
                 run.score(dev.q_idx, dev.kidx)
             elif stage == "select":
-                run.select()
+                run.select(kv_k) if (decode or query_major) else run.select()
             elif stage == "attend":
                 run.attend(dev.q, kv_k, kv_v, dev.scale)
             elif stage == "select_attend":

@@ -74,6 +74,15 @@ def _ptr(t, dtype, name: str, allow_none: bool = False) -> Optional[int]:
     return t.data_ptr()
 
 
+def _base(t, name: str) -> int:
+    """Base address of a strided view (the call's strides say how it is walked)."""
+    if isinstance(t, HostResident):
+        return _ptr(t, torch.bfloat16, name)
+    if not t.is_cuda or t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be a bf16 GPU tensor")
+    return t.data_ptr()
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -81,10 +90,24 @@ def _stream(stream) -> Optional[int]:
 
 
 def _cache(t, name: str) -> MsaCache:
+    """A paged cache [pages, block, heads, dim] whose token rows are contiguous.  The pages may be spaced
+    apart (a view such as pool[:, 0] of a [pages, 2, block, heads, dim] pool): the page dimension's
+    stride becomes the cache's page_stride."""
     if t.dim() != 4:
         raise ValueError(f"{name} must be [pages, block, heads, dim]")
     P, BS, H, D = t.shape
-    return MsaCache(_ptr(t, torch.bfloat16, name), P, BS, H, D)
+    if isinstance(t, HostResident):
+        return MsaCache(_ptr(t, torch.bfloat16, name), P, BS, H, D, 0)
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be {torch.bfloat16}, got {t.dtype}")
+    s = t.stride()
+    if s[3] != 1 or s[2] != D or s[1] != H * D:
+        raise ValueError(f"{name}: each page's [block, heads, dim] elements must be contiguous (only the page "
+                         f"dimension may be strided), got strides {tuple(s)}")
+    page_stride = 0 if (P == 1 or s[0] == BS * H * D) else s[0]
+    return MsaCache(t.data_ptr(), P, BS, H, D, page_stride)
 
 
 class Batch:
@@ -141,19 +164,20 @@ def msa_topk_blocks(batch: Batch, num_kv_heads: int, scores, k: int, sel, cnt, s
                                                      _stream(stream)))
 
 
-def msa_build_sparse_page_table(batch: Batch, num_kv_heads: int, num_pages: int, sel, cnt, k: int, page_table,
-                                row_len, stream=None) -> None:
+def msa_build_sparse_page_table(batch: Batch, kv_layout, sel, cnt, k: int, page_table, row_len, stream=None) -> None:
+    """kv_layout: the K (or V) cache tensor; only its shape and page stride are used."""
     check("msa_build_sparse_page_table",
-          load().msa_build_sparse_page_table(batch.ref(), num_kv_heads, num_pages, _ptr(sel, torch.int32, "sel"),
+          load().msa_build_sparse_page_table(batch.ref(), _cache(kv_layout, "kv_layout"), _ptr(sel, torch.int32, "sel"),
                                              _ptr(cnt, torch.int32, "cnt"), k,
                                              _ptr(page_table, torch.int32, "page_table"),
                                              _ptr(row_len, torch.int32, "row_len"), _stream(stream)))
 
 
-def msa_topk_page_table(batch: Batch, num_kv_heads: int, num_pages: int, scores, k: int, sel, cnt, page_table,
-                        row_len, stream=None) -> None:
+def msa_topk_page_table(batch: Batch, kv_layout, scores, k: int, sel, cnt, page_table, row_len, stream=None) -> None:
+    """kv_layout: the K (or V) cache tensor; only its shape and page stride are used."""
     check("msa_topk_page_table",
-          load().msa_topk_page_table(batch.ref(), num_kv_heads, num_pages, _ptr(scores, torch.float32, "scores"), k,
+          load().msa_topk_page_table(batch.ref(), _cache(kv_layout, "kv_layout"), _ptr(scores, torch.float32, "scores"),
+                                     k,
                                      _ptr(sel, torch.int32, "sel"), _ptr(cnt, torch.int32, "cnt"),
                                      _ptr(page_table, torch.int32, "page_table"),
                                      _ptr(row_len, torch.int32, "row_len"), _stream(stream)))
@@ -191,8 +215,8 @@ def msa_sparse_attn_decode_workspace_size(rows: int, G: int, D: int, k: int) -> 
 def msa_sparse_attn_decode(rows: int, G: int, D: int, q, k_base, v_base, page_stride: int, token_stride: int,
                            page_table, k: int, row_len, sm_scale: float, out, lse, workspace, stream=None) -> None:
     check("msa_sparse_attn_decode",
-          load().msa_sparse_attn_decode(rows, G, D, _ptr(q, torch.bfloat16, "q"), _ptr(k_base, torch.bfloat16, "k"),
-                                        _ptr(v_base, torch.bfloat16, "v"), page_stride, token_stride,
+          load().msa_sparse_attn_decode(rows, G, D, _ptr(q, torch.bfloat16, "q"), _base(k_base, "k_base"),
+                                        _base(v_base, "v_base"), page_stride, token_stride,
                                         _ptr(page_table, torch.int32, "page_table"), k,
                                         _ptr(row_len, torch.int32, "row_len"), sm_scale,
                                         _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse", True),

@@ -28,7 +28,7 @@ class MsaBatch(ctypes.Structure):
 
 class MsaCache(ctypes.Structure):
     _fields_ = [("data", c_vp), ("num_pages", c_i32), ("block_size", c_i32), ("num_heads", c_i32),
-                ("head_dim", c_i32)]
+                ("head_dim", c_i32), ("page_stride", c_i64)]
 
 
 _SIGS = {
@@ -36,9 +36,9 @@ _SIGS = {
     "msa_topk_blocks": (c_i32, [ctypes.POINTER(MsaBatch), c_i32, c_vp, c_i32, c_vp, c_vp, c_vp]),
     "msa_index_topk": (c_i32, [ctypes.POINTER(MsaBatch), c_vp, MsaCache, c_i32, c_vp, c_vp, c_vp, c_size, c_vp]),
     "msa_index_topk_workspace_size": (c_size, [ctypes.POINTER(MsaBatch), c_i32, c_i32]),
-    "msa_build_sparse_page_table": (c_i32, [ctypes.POINTER(MsaBatch), c_i32, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp,
+    "msa_build_sparse_page_table": (c_i32, [ctypes.POINTER(MsaBatch), MsaCache, c_vp, c_vp, c_i32, c_vp, c_vp,
                                             c_vp]),
-    "msa_topk_page_table": (c_i32, [ctypes.POINTER(MsaBatch), c_i32, c_i32, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp,
+    "msa_topk_page_table": (c_i32, [ctypes.POINTER(MsaBatch), MsaCache, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp,
                                     c_vp]),
     "msa_topk_attn_decode": (c_i32, [ctypes.POINTER(MsaBatch), c_vp, c_i32, MsaCache, MsaCache, c_i32, c_vp, c_f32,
                                      c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),

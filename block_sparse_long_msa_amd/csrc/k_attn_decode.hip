@@ -368,14 +368,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_decode(
 // the row's selection, count, page table and row length; then every split attends to its run of
 // pages exactly as k_attn_decode does.  The row's few hundred scores are read by each of its splits
 // instead of once, which costs far less than the launch and the page-table round trip it saves.
-// Caches [pages, 128, Hkv, D]: the view of KV head g has page stride D and token stride Hkv*D, and
-// the virtual page of physical page p is p*128*Hkv + g.
+// Caches of 128-token pages with Hkv*D-element token rows, page p at p*P elements: the view of KV head
+// g has page stride D and token stride Hkv*D, and the virtual page of physical page p is p*vps + g
+// with vps = P / D (128*Hkv for back-to-back pages).
 template <int D, int R>  // R scores per thread: max_blocks <= 256*R
 __global__ __launch_bounds__(256, 2) void k_select_attend(
     int B, int Hkv, int max_blocks, const int32_t* __restrict__ block_table, const int32_t* __restrict__ ctx_len,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ q_pos, const float* __restrict__ scores, int k,
     int32_t* __restrict__ sel, int32_t* __restrict__ cnt, int32_t* __restrict__ page_table,
-    int32_t* __restrict__ row_len, int G, const bf16* __restrict__ q, const bf16* __restrict__ kcache,
+    int32_t* __restrict__ row_len, int vps, int G, const bf16* __restrict__ q, const bf16* __restrict__ kcache,
     const bf16* __restrict__ vcache, float scale_log2, int ppw, int nsplit, bf16* __restrict__ out,
     float* __restrict__ lse_out, float* __restrict__ ws_o, float* __restrict__ ws_lse,
     uint32_t* __restrict__ counters) {
@@ -401,7 +402,7 @@ __global__ __launch_bounds__(256, 2) void k_select_attend(
 
   const int c = row_topk<NW, R>(v, n, k, sh, [&](int slot, int id, int r) {
     s_sel[slot] = id;
-    s_pt[slot] = bt[r] * (kBlock * Hkv) + g;
+    s_pt[slot] = bt[r] * vps + g;
   });
   __syncthreads();
   if (wv == 0) {
@@ -638,9 +639,10 @@ int select_attend_max_blocks() { return 256 * 16; }
 // at most select_attend_max_blocks().  Same splits, pages and arithmetic as the separate calls.
 hipError_t launch_select_attend(int B, int Nq, int Hkv, int max_blocks, const int32_t* block_table,
                                 const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const float* scores,
-                                int k, int32_t* sel, int32_t* cnt, int32_t* page_table, int32_t* row_len, int G, int D,
-                                const void* q, const void* kcache, const void* vcache, float sm_scale, void* out,
-                                float* lse, float* ws_o, float* ws_lse, uint32_t* counters, hipStream_t stream) {
+                                int k, int32_t* sel, int32_t* cnt, int32_t* page_table, int32_t* row_len, int vps,
+                                int G, int D, const void* q, const void* kcache, const void* vcache, float sm_scale,
+                                void* out, float* lse, float* ws_o, float* ws_lse, uint32_t* counters,
+                                hipStream_t stream) {
   const int rows = Nq * Hkv;
   const int nsplit = decode_splits(rows, k);
   const int ppw = (k + nsplit - 1) / nsplit;
@@ -653,7 +655,7 @@ hipError_t launch_select_attend(int B, int Nq, int Hkv, int max_blocks, const in
   bf16* oo = static_cast<bf16*>(out);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, block, 0, stream, B, Hkv, max_blocks, block_table, ctx_len, cu_q, q_pos, scores, k,
-                       sel, cnt, page_table, row_len, G, qq, kc, vc, sl2, ppw, nsplit, oo, lse, ws_o, ws_lse,
+                       sel, cnt, page_table, row_len, vps, G, qq, kc, vc, sl2, ppw, nsplit, oo, lse, ws_o, ws_lse,
                        fused ? counters : nullptr);
   };
   const int r = max_blocks <= 256 ? 1 : max_blocks <= 512 ? 2 : max_blocks <= 1024 ? 4 : max_blocks <= 2048 ? 8 : 16;

@@ -378,9 +378,10 @@ template <int D>
 __global__ __launch_bounds__(kThreads, MSA_KVBM_OCC) void k_attn_kvbm(
     int B, int Hkv, int G, int k, int max_blocks, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q,
-    const bf16* __restrict__ kcache, const bf16* __restrict__ vcache, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ item_off, const int2* __restrict__ items, const int32_t* __restrict__ entries,
-    int64_t NB, int chunk, float scale_log2, bf16* __restrict__ part_o, float* __restrict__ part_lse) {
+    const bf16* __restrict__ kcache, const bf16* __restrict__ vcache, int64_t kvpage,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ item_off, const int2* __restrict__ items,
+    const int32_t* __restrict__ entries, int64_t NB, int chunk, float scale_log2, bf16* __restrict__ part_o,
+    float* __restrict__ part_lse) {
   constexpr int KW = D / 32;        // 32-wide k windows over the head dimension
   constexpr int KS = kBlock / 32;   // 32-token k steps of the PV contraction
   constexpr int PAD = 8;            // LDS row padding (elements)
@@ -415,8 +416,8 @@ __global__ __launch_bounds__(kThreads, MSA_KVBM_OCC) void k_attn_kvbm(
   // exists instead: every load is in bounds and unconditional, so all of them are in flight at
   // once, and the values are finite.  Those keys are masked for every query row (lim <= in_block),
   // so their scores never count and their V rows are weighted by exactly 0.
-  const bf16* kg = kcache + ((int64_t)page * kBlock * Hkv + g) * D;
-  const bf16* vg = vcache + ((int64_t)page * kBlock * Hkv + g) * D;
+  const bf16* kg = kcache + (int64_t)page * kvpage + (int64_t)g * D;
+  const bf16* vg = vcache + (int64_t)page * kvpage + (int64_t)g * D;
   const int tstride = Hkv * D;
   static_assert(kBlock * D / 16 % kThreads == 0, "staging assumes whole rounds of 16-byte loads");
   constexpr int NKL = kBlock * D / 8 / kThreads, NVL = kBlock * D / 16 / kThreads;
@@ -636,7 +637,8 @@ hipError_t launch_tile_prep(int64_t rows, int B, int Hkv, int k, int G, int max_
                             hipStream_t stream);
 hipError_t launch_attn_tiles(int64_t max_tiles, int B, int Hkv, int G, int D, int k, int max_blocks, int H,
                              const int32_t* block_table, const int32_t* ctx_len, const int32_t* q_pos, const void* q,
-                             const void* kcache, const void* vcache, const int32_t* sel, const int32_t* hoffsets,
+                             const void* kcache, const void* vcache, int64_t kvpage, const int32_t* sel,
+                             const int32_t* hoffsets,
                              const int32_t* sorted_rows, const uint16_t* dense, const int32_t* dense_n,
                              const uint64_t* cov_mask, const int32_t* row_jt, const int2* tiles,
                              const int32_t* tile_count, float scale_log2, void* part_o, float* part_lse,
@@ -653,8 +655,8 @@ bool prefill_uses_tiles(int tile_min_rows, int G, int D, int max_blocks, int k) 
 hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blocks, int max_q,
                                const int32_t* block_table, const int32_t* ctx_len, const int32_t* cu_q,
                                const int32_t* q_pos, const void* q, const void* kcache, const void* vcache,
-                               const int32_t* sel, const int32_t* cnt, int k, float sm_scale, int tile_min_rows,
-                               void* part_o, float* part_lse, int32_t* slot_of, void* workspace,
+                               int64_t kvpage, const int32_t* sel, const int32_t* cnt, int k, float sm_scale,
+                               int tile_min_rows, void* part_o, float* part_lse, int32_t* slot_of, void* workspace,
                                hipStream_t stream) {
   const PrefillDims d = prefill_dims(Nq, Hkv, k, B, max_blocks, max_q);
   const int64_t NB = d.NB, E = d.E;
@@ -706,7 +708,7 @@ hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blo
   const float sl2 = sm_scale * kLog2eP;
   if (tiles) {
     hipError_t e = launch_attn_tiles(d.max_tiles, B, Hkv, G, D, k, max_blocks, d.H, block_table, ctx_len, q_pos, q,
-                                     kcache, vcache, sel, ws.hoffsets, ws.sorted_rows, ws.dense, ws.dense_n,
+                                     kcache, vcache, kvpage, sel, ws.hoffsets, ws.sorted_rows, ws.dense, ws.dense_n,
                                      ws.cov_mask, ws.row_jt, ws.tiles, ws.tile_count, sl2, part_o, part_lse, stream);
     if (e != hipSuccess) return e;
   }
@@ -719,12 +721,12 @@ hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blo
   bf16* po = static_cast<bf16*>(part_o);
   if (D == 128)
     hipLaunchKernelGGL(k_attn_kvbm<128>, dim3(grid), dim3(kThreads), 0, stream, B, Hkv, G, k, max_blocks, block_table,
-                       ctx_len, q_pos, qq, kc, vc, ws.offsets, ws.item_off, ws.items, ws.entries, NB, chunk, sl2, po,
-                       part_lse);
+                       ctx_len, q_pos, qq, kc, vc, kvpage, ws.offsets, ws.item_off, ws.items, ws.entries, NB, chunk,
+                       sl2, po, part_lse);
   else
     hipLaunchKernelGGL(k_attn_kvbm<64>, dim3(grid), dim3(kThreads), 0, stream, B, Hkv, G, k, max_blocks, block_table,
-                       ctx_len, q_pos, qq, kc, vc, ws.offsets, ws.item_off, ws.items, ws.entries, NB, chunk, sl2, po,
-                       part_lse);
+                       ctx_len, q_pos, qq, kc, vc, kvpage, ws.offsets, ws.item_off, ws.items, ws.entries, NB, chunk,
+                       sl2, po, part_lse);
   return hipGetLastError();
 }
 

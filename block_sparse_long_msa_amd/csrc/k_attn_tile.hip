@@ -264,7 +264,7 @@ template <int D, int G>
 __global__ __launch_bounds__(kTileThreads, 1) void k_attn_tile(
     int B, int Hkv, int k, int max_blocks, int H, const int32_t* __restrict__ block_table,
     const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q,
-    const bf16* __restrict__ kcache, const bf16* __restrict__ vcache, const int32_t* __restrict__ sel,
+    const bf16* __restrict__ kcache, const bf16* __restrict__ vcache, int64_t kvpage, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ hoffsets, const int32_t* __restrict__ sorted_rows,
     const uint16_t* __restrict__ dense, const int32_t* __restrict__ dense_n, const uint64_t* __restrict__ cov_mask,
     const int32_t* __restrict__ row_jt, const int2* __restrict__ tiles, const int32_t* __restrict__ tile_count,
@@ -360,8 +360,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_attn_tile(
     const int b = __builtin_amdgcn_readfirstlane(s_union[sc >> 1]), hf = sc & 1;
     const int page = block_table[(int64_t)r * max_blocks + b];
     const int in_block = min(kBlock, L - b * kBlock);
-    const bf16* kg = kcache + ((int64_t)page * kBlock * Hkv + g) * D;
-    const bf16* vg = vcache + ((int64_t)page * kBlock * Hkv + g) * D;
+    const bf16* kg = kcache + (int64_t)page * kvpage + (int64_t)g * D;
+    const bf16* vg = vcache + (int64_t)page * kvpage + (int64_t)g * D;
     const int buf = s % RING;
 #pragma unroll
     for (int i = 0; i < NIH; ++i) {
@@ -643,11 +643,11 @@ hipError_t launch_tile_prep(int64_t rows, int B, int Hkv, int k, int G, int max_
 
 hipError_t launch_attn_tiles(int64_t max_tiles, int B, int Hkv, int G, int D, int k, int max_blocks, int H,
                              const int32_t* block_table, const int32_t* ctx_len, const int32_t* q_pos, const void* q,
-                             const void* kcache, const void* vcache, const int32_t* sel, const int32_t* hoffsets,
-                             const int32_t* sorted_rows, const uint16_t* dense, const int32_t* dense_n,
-                             const uint64_t* cov_mask, const int32_t* row_jt, const int2* tiles,
-                             const int32_t* tile_count, float scale_log2, void* part_o, float* part_lse,
-                             hipStream_t stream) {
+                             const void* kcache, const void* vcache, int64_t kvpage, const int32_t* sel,
+                             const int32_t* hoffsets, const int32_t* sorted_rows, const uint16_t* dense,
+                             const int32_t* dense_n, const uint64_t* cov_mask, const int32_t* row_jt,
+                             const int2* tiles, const int32_t* tile_count, float scale_log2, void* part_o,
+                             float* part_lse, hipStream_t stream) {
   const unsigned grid = (unsigned)max_tiles;
   if (grid == 0) return hipSuccess;
   const bf16* qq = static_cast<const bf16*>(q);
@@ -656,8 +656,8 @@ hipError_t launch_attn_tiles(int64_t max_tiles, int B, int Hkv, int G, int D, in
   bf16* po = static_cast<bf16*>(part_o);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kTileThreads), 0, stream, B, Hkv, k, max_blocks, H, block_table,
-                       ctx_len, q_pos, qq, kc, vc, sel, hoffsets, sorted_rows, dense, dense_n, cov_mask, row_jt,
-                       tiles, tile_count, scale_log2, po, part_lse);
+                       ctx_len, q_pos, qq, kc, vc, kvpage, sel, hoffsets, sorted_rows, dense, dense_n, cov_mask,
+                       row_jt, tiles, tile_count, scale_log2, po, part_lse);
   };
   if (D == 128) {
     if (G == 4) go(k_attn_tile<128, 4>);

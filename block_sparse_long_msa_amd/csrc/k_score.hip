@@ -60,7 +60,7 @@ template <int DI>
 __global__ __launch_bounds__(256) void k_score_decode(
     const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ ctx_len,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q_idx,
-    const bf16* __restrict__ kidx, int Hkv, float* __restrict__ scores) {
+    const bf16* __restrict__ kidx, int Hkv, int64_t kpage, float* __restrict__ scores) {
   constexpr int KW = DI / 32;
   constexpr int PF = MSA_SCORE_PREFETCH;  // KV heads in flight ahead of the one being multiplied
   __shared__ float red[4][64][16];
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void k_score_decode(
     }
     const int page = block_table[(int64_t)r * max_blocks + b];
     // lane (n, qd): A rows are tokens 32w + 16sub + n, k chunk 8qd within each 32-wide window
-    const bf16* ka = kidx + ((int64_t)page * kBlock + 32 * w + n) * Hkv * DI + 8 * qd;
+    const bf16* ka = kidx + (int64_t)page * kpage + (int64_t)(32 * w + n) * Hkv * DI + 8 * qd;
     const bf16* qa = q_idx + (int64_t)my_t * Hkv * DI + 8 * qd;
     const int tok_base = b * kBlock + 32 * w + 4 * qd;
 
@@ -152,7 +152,7 @@ template <int DI>
 __global__ __launch_bounds__(256, 2) void k_score_decode_lds(
     const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ ctx_len,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q_idx,
-    const bf16* __restrict__ kidx, int Hkv, float* __restrict__ scores) {
+    const bf16* __restrict__ kidx, int Hkv, int64_t kpage, float* __restrict__ scores) {
   constexpr int KW = DI / 32;
   constexpr int GPW = 256 / DI;           // KV heads per wave at most (Hkv * DI <= 1024)
   constexpr int LPT = kStageBytes / 16 / 256;  // 16-byte loads per thread per slice (8)
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void k_score_decode_lds(
     int pg = page[0];
 #pragma unroll
     for (int j = 1; j < kScoreBPW; ++j) pg = bi == j ? page[j] : pg;
-    return reinterpret_cast<const unsigned char*>(kidx) + ((int64_t)pg * kBlock * RB + (int64_t)sl * slice_bytes);
+    return reinterpret_cast<const unsigned char*>(kidx) + ((int64_t)pg * kpage * 2 + (int64_t)sl * slice_bytes);
   };
   auto load_slice = [&](u32x4 (&reg)[LPT], int gs) {
     const unsigned char* src = slice_src(min(gs, S - 1));
@@ -357,7 +357,8 @@ template <int DI, int TOPK, int W>
 __global__ __launch_bounds__(64 * W, 8 / W) void k_score_prefill(
     int B, int Nq, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ ctx_len,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ q_pos, const bf16* __restrict__ q_idx,
-    const bf16* __restrict__ kidx, int Hkv, float* __restrict__ scores, int k, int32_t* __restrict__ sel,
+    const bf16* __restrict__ kidx, int Hkv, int64_t kpage, float* __restrict__ scores, int k,
+    int32_t* __restrict__ sel,
     int32_t* __restrict__ cnt, int nsplit) {
   constexpr int kPrefThreads = 64 * W;
   constexpr int kPrefTQ = kPrefThreads;  // query rows per workgroup (64 per wave, one per thread)
@@ -446,7 +447,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void k_score_prefill(
     // state an LDS DMA needs after m0 is written, and one more before m0 is written back.
     auto issue_block = [&](int bb, int buf) {
       const int page = block_table[(int64_t)r * max_blocks + bb];
-      const bf16* kb = kidx + ((int64_t)page * kBlock * Hkv + g) * DI;
+      const bf16* kb = kidx + (int64_t)page * kpage + (int64_t)g * DI;
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i) {
         const int grp = W * i + w;                         // wave-uniform group of 64 chunks
@@ -578,7 +579,7 @@ __global__ __launch_bounds__(64 * W, 8 / W) void k_score_prefill(
 
 hipError_t launch_score_decode(int B, int Di, const int32_t* block_table, int max_blocks, const int32_t* ctx_len,
                                const int32_t* cu_q, const int32_t* q_pos, const void* q_idx, const void* kidx,
-                               int Hkv, float* scores, hipStream_t stream) {
+                               int Hkv, int64_t kpage, float* scores, hipStream_t stream) {
   dim3 grid(max_blocks, B), block(256);
   const bf16* qi = static_cast<const bf16*>(q_idx);
   const bf16* ki = static_cast<const bf16*>(kidx);
@@ -586,18 +587,18 @@ hipError_t launch_score_decode(int B, int Di, const int32_t* block_table, int ma
     grid.x = (max_blocks + kScoreBPW - 1) / kScoreBPW;
     if (Di == 128)
       hipLaunchKernelGGL(k_score_decode_lds<128>, grid, block, 0, stream, block_table, max_blocks, ctx_len, cu_q,
-                         q_pos, qi, ki, Hkv, scores);
+                         q_pos, qi, ki, Hkv, kpage, scores);
     else
       hipLaunchKernelGGL(k_score_decode_lds<64>, grid, block, 0, stream, block_table, max_blocks, ctx_len, cu_q,
-                         q_pos, qi, ki, Hkv, scores);
+                         q_pos, qi, ki, Hkv, kpage, scores);
     return hipGetLastError();
   }
   if (Di == 128)
     hipLaunchKernelGGL(k_score_decode<128>, grid, block, 0, stream, block_table, max_blocks, ctx_len, cu_q, q_pos,
-                       qi, ki, Hkv, scores);
+                       qi, ki, Hkv, kpage, scores);
   else
     hipLaunchKernelGGL(k_score_decode<64>, grid, block, 0, stream, block_table, max_blocks, ctx_len, cu_q, q_pos,
-                       qi, ki, Hkv, scores);
+                       qi, ki, Hkv, kpage, scores);
   return hipGetLastError();
 }
 
@@ -626,7 +627,7 @@ void launch_prefill(int Di, dim3 grid, hipStream_t stream, Args... args) {
 
 hipError_t launch_score_prefill(int B, int Nq, int Di, const int32_t* block_table, int max_blocks,
                                 const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const void* q_idx,
-                                const void* kidx, int Hkv, float* scores, hipStream_t stream) {
+                                const void* kidx, int Hkv, int64_t kpage, float* scores, hipStream_t stream) {
   const PrefillShape sh = prefill_shape(Nq, Hkv);
   // Few row tiles (short prompts): cut each tile's blocks into runs, doubling the runs while the
   // launch stays within kPrefTargetWgs workgroups and there are blocks for every run.
@@ -638,10 +639,10 @@ hipError_t launch_score_prefill(int B, int Nq, int Di, const int32_t* block_tabl
   int32_t* none = nullptr;
   if (sh.waves == kPrefWideW)
     launch_prefill<0, kPrefWideW>(Di, grid, stream, B, Nq, block_table, max_blocks, ctx_len, cu_q, q_pos, qi, ki, Hkv,
-                                  scores, 0, none, none, nsplit);
+                                  kpage, scores, 0, none, none, nsplit);
   else
     launch_prefill<0, kPrefNarrowW>(Di, grid, stream, B, Nq, block_table, max_blocks, ctx_len, cu_q, q_pos, qi, ki,
-                                    Hkv, scores, 0, none, none, nsplit);
+                                    Hkv, kpage, scores, 0, none, none, nsplit);
   return hipGetLastError();
 }
 
@@ -649,8 +650,8 @@ int fused_topk_capacity() { return kFusedTopK; }
 
 hipError_t launch_score_topk_prefill(int B, int Nq, int Di, const int32_t* block_table, int max_blocks,
                                      const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos,
-                                     const void* q_idx, const void* kidx, int Hkv, int k, int32_t* sel, int32_t* cnt,
-                                     hipStream_t stream) {
+                                     const void* q_idx, const void* kidx, int Hkv, int64_t kpage, int k, int32_t* sel,
+                                     int32_t* cnt, hipStream_t stream) {
   const PrefillShape sh = prefill_shape(Nq, Hkv);
   const dim3 grid(sh.tiles * Hkv);
   const bf16* qi = static_cast<const bf16*>(q_idx);
@@ -658,10 +659,10 @@ hipError_t launch_score_topk_prefill(int B, int Nq, int Di, const int32_t* block
   float* none = nullptr;
   if (sh.waves == kPrefWideW)
     launch_prefill<kFusedTopK, kPrefWideW>(Di, grid, stream, B, Nq, block_table, max_blocks, ctx_len, cu_q, q_pos,
-                                           qi, ki, Hkv, none, k, sel, cnt, 1);
+                                           qi, ki, Hkv, kpage, none, k, sel, cnt, 1);
   else
     launch_prefill<kFusedTopK, kPrefNarrowW>(Di, grid, stream, B, Nq, block_table, max_blocks, ctx_len, cu_q, q_pos,
-                                             qi, ki, Hkv, none, k, sel, cnt, 1);
+                                             qi, ki, Hkv, kpage, none, k, sel, cnt, 1);
   return hipGetLastError();
 }
 

@@ -170,6 +170,7 @@ struct PageTableOut {
   const int32_t* cu_q;
   int32_t* page_table;  // NULL: top-k only
   int32_t* row_len;
+  int vps;              // virtual pages per physical page: the cache's page stride / D
 };
 
 template <int NW, int R>
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(64 * NW) void k_topk_reg(int Hkv, int max_blocks, c
       int pv = -1, len = 0;
       if (lane < c) {
         const int bl = s_sel[lane];
-        pv = pto.block_table[(int64_t)r_req * max_blocks + bl] * (kBlock * Hkv) + g;
+        pv = pto.block_table[(int64_t)r_req * max_blocks + bl] * pto.vps + g;
         len = min(kBlock, lim - bl * kBlock);
       }
       if (lane < k) pto.page_table[(int64_t)row * k + lane] = pv;
@@ -226,14 +227,15 @@ __global__ __launch_bounds__(64 * NW) void k_topk_reg(int Hkv, int max_blocks, c
 }
 
 // Decode sparse page table over the strided view (Chinese page, section "MSA需要新的分页注意力集成"):
-// row rho = t*Hkv + g, page_table[rho, j] = block_table[r, sel[t,g,j]] * 128 * Hkv + g.
+// row rho = t*Hkv + g, page_table[rho, j] = block_table[r, sel[t,g,j]] * vps + g, vps = the cache's
+// page stride / D (128 * Hkv for back-to-back pages).
 // One wavefront per row; lane j handles slot j (k <= 64), row_len is a wave sum.
 __global__ __launch_bounds__(256) void k_page_table(int rows, int B, int Hkv, int max_blocks,
                                                     const int32_t* __restrict__ block_table,
                                                     const int32_t* __restrict__ ctx_len,
                                                     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ q_pos,
                                                     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
-                                                    int k, int32_t* __restrict__ page_table,
+                                                    int k, int vps, int32_t* __restrict__ page_table,
                                                     int32_t* __restrict__ row_len) {
   const int rho = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int j = threadIdx.x & 63;
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(256) void k_page_table(int rows, int B, int Hkv, in
   int v = -1, len = 0;
   if (j < c) {
     const int bl = sel[(int64_t)rho * k + j];
-    v = block_table[(int64_t)r * max_blocks + bl] * (kBlock * Hkv) + g;
+    v = block_table[(int64_t)r * max_blocks + bl] * vps + g;
     len = min(kBlock, lim - bl * kBlock);
   }
   if (j < k) page_table[(int64_t)rho * k + j] = v;
@@ -288,7 +290,7 @@ static bool launch_topk_reg(int rows, int Hkv, int max_blocks, const int32_t* q_
 hipError_t launch_topk(int B, int Nq, int Hkv, int max_blocks, const int32_t* cu_q, const int32_t* q_pos,
                        const float* scores, int k, int32_t* sel, int32_t* cnt, hipStream_t stream) {
   const int rows = Nq * Hkv;
-  const PageTableOut none{B, nullptr, nullptr, cu_q, nullptr, nullptr};
+  const PageTableOut none{B, nullptr, nullptr, cu_q, nullptr, nullptr, 0};
   if (launch_topk_reg(rows, Hkv, max_blocks, q_pos, scores, k, sel, cnt, none, stream)) return hipGetLastError();
   // rows longer than the register layouts: radix passes, 16 waves per row when the rows are few
   if (rows < 4096)
@@ -302,22 +304,23 @@ hipError_t launch_topk(int B, int Nq, int Hkv, int max_blocks, const int32_t* cu
 
 hipError_t launch_page_table(int B, int Nq, int Hkv, int max_blocks, const int32_t* block_table,
                              const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const int32_t* sel,
-                             const int32_t* cnt, int k, int32_t* page_table, int32_t* row_len, hipStream_t stream) {
+                             const int32_t* cnt, int k, int vps, int32_t* page_table, int32_t* row_len,
+                             hipStream_t stream) {
   const int rows = Nq * Hkv;
   hipLaunchKernelGGL(k_page_table, dim3((rows + 3) / 4), dim3(256), 0, stream, rows, B, Hkv, max_blocks,
-                     block_table, ctx_len, cu_q, q_pos, sel, cnt, k, page_table, row_len);
+                     block_table, ctx_len, cu_q, q_pos, sel, cnt, k, vps, page_table, row_len);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_page_table(int B, int Nq, int Hkv, int max_blocks, const int32_t* block_table,
                                   const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos,
-                                  const float* scores, int k, int32_t* sel, int32_t* cnt, int32_t* page_table,
-                                  int32_t* row_len, hipStream_t stream) {
-  const PageTableOut pto{B, block_table, ctx_len, cu_q, page_table, row_len};
+                                  const float* scores, int k, int32_t* sel, int32_t* cnt, int vps,
+                                  int32_t* page_table, int32_t* row_len, hipStream_t stream) {
+  const PageTableOut pto{B, block_table, ctx_len, cu_q, page_table, row_len, vps};
   if (launch_topk_reg(Nq * Hkv, Hkv, max_blocks, q_pos, scores, k, sel, cnt, pto, stream)) return hipGetLastError();
   hipError_t e = launch_topk(B, Nq, Hkv, max_blocks, cu_q, q_pos, scores, k, sel, cnt, stream);
   if (e != hipSuccess) return e;
-  return launch_page_table(B, Nq, Hkv, max_blocks, block_table, ctx_len, cu_q, q_pos, sel, cnt, k, page_table,
+  return launch_page_table(B, Nq, Hkv, max_blocks, block_table, ctx_len, cu_q, q_pos, sel, cnt, k, vps, page_table,
                            row_len, stream);
 }
 

@@ -11,31 +11,33 @@
 namespace msa {
 hipError_t launch_score_decode(int B, int Di, const int32_t* block_table, int max_blocks, const int32_t* ctx_len,
                                const int32_t* cu_q, const int32_t* q_pos, const void* q_idx, const void* kidx,
-                               int Hkv, float* scores, hipStream_t stream);
+                               int Hkv, int64_t kpage, float* scores, hipStream_t stream);
 hipError_t launch_score_prefill(int B, int Nq, int Di, const int32_t* block_table, int max_blocks,
                                 const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const void* q_idx,
-                                const void* kidx, int Hkv, float* scores, hipStream_t stream);
+                                const void* kidx, int Hkv, int64_t kpage, float* scores, hipStream_t stream);
 int fused_topk_capacity();
 hipError_t launch_score_topk_prefill(int B, int Nq, int Di, const int32_t* block_table, int max_blocks,
                                      const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos,
-                                     const void* q_idx, const void* kidx, int Hkv, int k, int32_t* sel, int32_t* cnt,
-                                     hipStream_t stream);
+                                     const void* q_idx, const void* kidx, int Hkv, int64_t kpage, int k, int32_t* sel,
+                                     int32_t* cnt, hipStream_t stream);
 hipError_t launch_topk(int B, int Nq, int Hkv, int max_blocks, const int32_t* cu_q, const int32_t* q_pos,
                        const float* scores, int k, int32_t* sel, int32_t* cnt, hipStream_t stream);
 hipError_t launch_page_table(int B, int Nq, int Hkv, int max_blocks, const int32_t* block_table,
                              const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const int32_t* sel,
-                             const int32_t* cnt, int k, int32_t* page_table, int32_t* row_len, hipStream_t stream);
+                             const int32_t* cnt, int k, int vps, int32_t* page_table, int32_t* row_len,
+                             hipStream_t stream);
 hipError_t launch_topk_page_table(int B, int Nq, int Hkv, int max_blocks, const int32_t* block_table,
                                   const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos,
-                                  const float* scores, int k, int32_t* sel, int32_t* cnt, int32_t* page_table,
-                                  int32_t* row_len, hipStream_t stream);
+                                  const float* scores, int k, int32_t* sel, int32_t* cnt, int vps,
+                                  int32_t* page_table, int32_t* row_len, hipStream_t stream);
 int decode_splits(int rows, int k);
 int select_attend_max_blocks();
 hipError_t launch_select_attend(int B, int Nq, int Hkv, int max_blocks, const int32_t* block_table,
                                 const int32_t* ctx_len, const int32_t* cu_q, const int32_t* q_pos, const float* scores,
-                                int k, int32_t* sel, int32_t* cnt, int32_t* page_table, int32_t* row_len, int G, int D,
-                                const void* q, const void* kcache, const void* vcache, float sm_scale, void* out,
-                                float* lse, float* ws_o, float* ws_lse, uint32_t* counters, hipStream_t stream);
+                                int k, int32_t* sel, int32_t* cnt, int32_t* page_table, int32_t* row_len, int vps,
+                                int G, int D, const void* q, const void* kcache, const void* vcache, float sm_scale,
+                                void* out, float* lse, float* ws_o, float* ws_lse, uint32_t* counters,
+                                hipStream_t stream);
 hipError_t launch_attn_decode(int rows, int G, int D, const void* q, const void* kview, const void* vview,
                               int64_t page_stride, int64_t token_stride, const int32_t* page_table, int k,
                               const int32_t* row_len, float sm_scale, void* out, float* lse, float* ws_o,
@@ -48,8 +50,8 @@ size_t prefill_workspace_bytes(int32_t Nq, int32_t Hkv, int32_t k, int32_t B, in
 hipError_t launch_attn_prefill(int B, int Nq, int Hkv, int G, int D, int max_blocks, int max_q,
                                const int32_t* block_table, const int32_t* ctx_len, const int32_t* cu_q,
                                const int32_t* q_pos, const void* q, const void* kcache, const void* vcache,
-                               const int32_t* sel, const int32_t* cnt, int k, float sm_scale, int tile_min_rows,
-                               void* part_o, float* part_lse, int32_t* slot_of, void* workspace,
+                               int64_t kvpage, const int32_t* sel, const int32_t* cnt, int k, float sm_scale,
+                               int tile_min_rows, void* part_o, float* part_lse, int32_t* slot_of, void* workspace,
                                hipStream_t stream);
 }  // namespace msa
 
@@ -102,15 +104,41 @@ msa_status check_batch(const msa_batch* b) {
   return MSA_OK;
 }
 
-msa_status check_cache(const msa_cache& c, const char* name) {
-  MSA_REQUIRE(c.data != nullptr, MSA_ERR_INVALID_ARG, "%s: data is NULL", name);
-  MSA_REQUIRE(aligned16(c.data), MSA_ERR_INVALID_ARG, "%s: data must be 16-byte aligned", name);
+// Elements from one page of the cache to the next.
+int64_t page_elems(const msa_cache& c) {
+  return c.page_stride ? c.page_stride : (int64_t)c.block_size * c.num_heads * c.head_dim;
+}
+
+// The cache's shape and page stride (data not read).
+msa_status check_layout(const msa_cache& c, const char* name) {
   MSA_REQUIRE(c.num_pages >= 1, MSA_ERR_INVALID_ARG, "%s: num_pages must be >= 1", name);
   MSA_REQUIRE(c.block_size == 128, MSA_ERR_UNSUPPORTED, "%s: block_size must be 128, got %d", name, c.block_size);
   MSA_REQUIRE(c.num_heads >= 1 && c.num_heads <= kMaxHkv, MSA_ERR_UNSUPPORTED, "%s: num_heads must be in [1, %d]",
               name, kMaxHkv);
   MSA_REQUIRE(supported_dim(c.head_dim), MSA_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128, got %d", name,
               c.head_dim);
+  const int64_t dense = (int64_t)c.block_size * c.num_heads * c.head_dim;
+  MSA_REQUIRE(c.page_stride == 0 || (c.page_stride >= dense && c.page_stride % 8 == 0), MSA_ERR_INVALID_ARG,
+              "%s: page_stride must be 0 or a multiple of 8 that is >= block_size*num_heads*head_dim = %lld, got %lld",
+              name, (long long)dense, (long long)c.page_stride);
+  return MSA_OK;
+}
+
+// A K or V cache: also the virtual page ids of the decode page table, page * (page_stride / head_dim)
+// + head, must be whole and fit in int32.
+msa_status check_kv_layout(const msa_cache& c, const char* name) {
+  if (msa_status s = check_layout(c, name)) return s;
+  MSA_REQUIRE(page_elems(c) % c.head_dim == 0, MSA_ERR_INVALID_ARG, "%s: page_stride must be a multiple of head_dim",
+              name);
+  MSA_REQUIRE((int64_t)c.num_pages * (page_elems(c) / c.head_dim) <= 0x7fffffffLL, MSA_ERR_UNSUPPORTED,
+              "%s: num_pages * page_stride / head_dim must fit in int32 (virtual page ids)", name);
+  return MSA_OK;
+}
+
+msa_status check_cache(const msa_cache& c, const char* name) {
+  MSA_REQUIRE(c.data != nullptr, MSA_ERR_INVALID_ARG, "%s: data is NULL", name);
+  MSA_REQUIRE(aligned16(c.data), MSA_ERR_INVALID_ARG, "%s: data must be 16-byte aligned", name);
+  if (msa_status s = check_layout(c, name)) return s;
   return MSA_OK;
 }
 
@@ -148,11 +176,11 @@ msa_status msa_index_score(const msa_batch* batch, const void* q_idx, msa_cache 
   if (batch->max_q_per_request <= 16)
     e = msa::launch_score_decode(batch->num_requests, k_idx.head_dim, batch->block_table, batch->max_blocks,
                                  batch->ctx_len, batch->cu_q, batch->q_pos, q_idx, k_idx.data, k_idx.num_heads,
-                                 scores, st);
+                                 page_elems(k_idx), scores, st);
   else
     e = msa::launch_score_prefill(batch->num_requests, batch->num_queries, k_idx.head_dim, batch->block_table,
                                   batch->max_blocks, batch->ctx_len, batch->cu_q, batch->q_pos, q_idx, k_idx.data,
-                                  k_idx.num_heads, scores, st);
+                                  k_idx.num_heads, page_elems(k_idx), scores, st);
   return from_hip(e, "msa_index_score launch");
 }
 
@@ -182,8 +210,8 @@ msa_status msa_index_topk(const msa_batch* batch, const void* q_idx, msa_cache k
   if (fused_index_topk(batch, k))
     return from_hip(msa::launch_score_topk_prefill(batch->num_requests, batch->num_queries, k_idx.head_dim,
                                                    batch->block_table, batch->max_blocks, batch->ctx_len,
-                                                   batch->cu_q, batch->q_pos, q_idx, k_idx.data, k_idx.num_heads, k,
-                                                   sel, cnt, st),
+                                                   batch->cu_q, batch->q_pos, q_idx, k_idx.data, k_idx.num_heads,
+                                                   page_elems(k_idx), k, sel, cnt, st),
                     "msa_index_topk launch");
   const size_t need = msa_index_topk_workspace_size(batch, k_idx.num_heads, k);
   MSA_REQUIRE(workspace && aligned16(workspace) && workspace_bytes >= need, MSA_ERR_WORKSPACE_TOO_SMALL,
@@ -212,50 +240,45 @@ msa_status msa_topk_blocks(const msa_batch* batch, int32_t num_kv_heads, const f
                   "msa_topk_blocks launch");
 }
 
-msa_status msa_build_sparse_page_table(const msa_batch* batch, int32_t num_kv_heads, int32_t num_pages,
-                                       const int32_t* sel, const int32_t* cnt, int32_t k, int32_t* page_table,
-                                       int32_t* row_len, msa_stream_t stream) {
+msa_status msa_build_sparse_page_table(const msa_batch* batch, msa_cache kv_layout, const int32_t* sel,
+                                       const int32_t* cnt, int32_t k, int32_t* page_table, int32_t* row_len,
+                                       msa_stream_t stream) {
   g_last_error.clear();
   if (msa_status s = check_batch(batch)) return s;
-  MSA_REQUIRE(num_kv_heads >= 1 && num_kv_heads <= kMaxHkv, MSA_ERR_UNSUPPORTED, "num_kv_heads must be in [1, %d]",
-              kMaxHkv);
+  if (msa_status s = check_kv_layout(kv_layout, "kv_layout")) return s;
+  const int Hkv = kv_layout.num_heads;
   MSA_REQUIRE(k >= 1 && k <= kMaxK, MSA_ERR_UNSUPPORTED, "k must be in [1, %d], got %d", kMaxK, k);
-  MSA_REQUIRE(num_pages >= 1, MSA_ERR_INVALID_ARG, "num_pages must be >= 1");
-  MSA_REQUIRE((int64_t)num_pages * 128 * num_kv_heads <= 0x7fffffffLL, MSA_ERR_UNSUPPORTED,
-              "num_pages*128*num_kv_heads must fit in int32 (virtual page ids)");
   MSA_REQUIRE(batch->num_queries == 0 || (sel && cnt && page_table && row_len), MSA_ERR_INVALID_ARG,
               "sel, cnt, page_table and row_len must be non-NULL");
   MSA_REQUIRE(aligned4(sel) && aligned4(cnt) && aligned4(page_table) && aligned4(row_len), MSA_ERR_INVALID_ARG,
               "arrays must be 4-byte aligned");
   if (batch->num_queries == 0) return MSA_OK;
-  return from_hip(msa::launch_page_table(batch->num_requests, batch->num_queries, num_kv_heads, batch->max_blocks,
+  return from_hip(msa::launch_page_table(batch->num_requests, batch->num_queries, Hkv, batch->max_blocks,
                                          batch->block_table, batch->ctx_len, batch->cu_q, batch->q_pos, sel, cnt, k,
-                                         page_table, row_len, reinterpret_cast<hipStream_t>(stream)),
+                                         (int)(page_elems(kv_layout) / kv_layout.head_dim), page_table, row_len,
+                                         reinterpret_cast<hipStream_t>(stream)),
                   "msa_build_sparse_page_table launch");
 }
 
-msa_status msa_topk_page_table(const msa_batch* batch, int32_t num_kv_heads, int32_t num_pages,
-                               const float* scores, int32_t k, int32_t* sel, int32_t* cnt, int32_t* page_table,
-                               int32_t* row_len, msa_stream_t stream) {
+msa_status msa_topk_page_table(const msa_batch* batch, msa_cache kv_layout, const float* scores, int32_t k,
+                               int32_t* sel, int32_t* cnt, int32_t* page_table, int32_t* row_len,
+                               msa_stream_t stream) {
   g_last_error.clear();
   if (msa_status s = check_batch(batch)) return s;
-  MSA_REQUIRE(num_kv_heads >= 1 && num_kv_heads <= kMaxHkv, MSA_ERR_UNSUPPORTED, "num_kv_heads must be in [1, %d]",
-              kMaxHkv);
+  if (msa_status s = check_kv_layout(kv_layout, "kv_layout")) return s;
+  const int Hkv = kv_layout.num_heads;
   MSA_REQUIRE(k >= 1 && k <= kMaxK, MSA_ERR_UNSUPPORTED, "k must be in [1, %d], got %d", kMaxK, k);
-  MSA_REQUIRE(num_pages >= 1, MSA_ERR_INVALID_ARG, "num_pages must be >= 1");
-  MSA_REQUIRE((int64_t)num_pages * 128 * num_kv_heads <= 0x7fffffffLL, MSA_ERR_UNSUPPORTED,
-              "num_pages*128*num_kv_heads must fit in int32 (virtual page ids)");
   MSA_REQUIRE(batch->num_queries == 0 || (scores && sel && cnt && page_table && row_len), MSA_ERR_INVALID_ARG,
               "scores, sel, cnt, page_table and row_len must be non-NULL");
   MSA_REQUIRE(aligned4(scores) && aligned4(sel) && aligned4(cnt) && aligned4(page_table) && aligned4(row_len),
               MSA_ERR_INVALID_ARG, "arrays must be 4-byte aligned");
-  MSA_REQUIRE((int64_t)batch->num_queries * num_kv_heads <= 0x7fffffff, MSA_ERR_UNSUPPORTED,
+  MSA_REQUIRE((int64_t)batch->num_queries * Hkv <= 0x7fffffff, MSA_ERR_UNSUPPORTED,
               "num_queries * num_kv_heads exceeds the grid limit");
   if (batch->num_queries == 0) return MSA_OK;
-  return from_hip(msa::launch_topk_page_table(batch->num_requests, batch->num_queries, num_kv_heads,
-                                              batch->max_blocks, batch->block_table, batch->ctx_len, batch->cu_q,
-                                              batch->q_pos, scores, k, sel, cnt, page_table, row_len,
-                                              reinterpret_cast<hipStream_t>(stream)),
+  return from_hip(msa::launch_topk_page_table(batch->num_requests, batch->num_queries, Hkv, batch->max_blocks,
+                                              batch->block_table, batch->ctx_len, batch->cu_q, batch->q_pos, scores,
+                                              k, sel, cnt, (int)(page_elems(kv_layout) / kv_layout.head_dim),
+                                              page_table, row_len, reinterpret_cast<hipStream_t>(stream)),
                   "msa_topk_page_table launch");
 }
 
@@ -337,14 +360,14 @@ msa_status topk_attn_decode(const msa_batch* batch, const float* scores, int32_t
   if (msa_status s = check_batch(batch)) return s;
   if (msa_status s = check_cache(k_cache, "k_cache")) return s;
   if (msa_status s = check_cache(v_cache, "v_cache")) return s;
+  if (msa_status s = check_kv_layout(k_cache, "k_cache")) return s;
   MSA_REQUIRE(k_cache.num_pages == v_cache.num_pages && k_cache.num_heads == v_cache.num_heads &&
-                  k_cache.head_dim == v_cache.head_dim,
-              MSA_ERR_INVALID_ARG, "k_cache and v_cache must have the same shape");
+                  k_cache.head_dim == v_cache.head_dim && page_elems(k_cache) == page_elems(v_cache),
+              MSA_ERR_INVALID_ARG, "k_cache and v_cache must have the same shape and page stride");
   const int Hkv = k_cache.num_heads, D = k_cache.head_dim;
+  const int vps = (int)(page_elems(k_cache) / D);  // virtual pages per page of the strided views
   MSA_REQUIRE(supported_group(G), MSA_ERR_UNSUPPORTED, "G must be 1, 2, 4, 8 or 16, got %d", G);
   MSA_REQUIRE(k >= 1 && k <= kMaxK, MSA_ERR_UNSUPPORTED, "k must be in [1, %d], got %d", kMaxK, k);
-  MSA_REQUIRE((int64_t)k_cache.num_pages * 128 * Hkv <= 0x7fffffffLL, MSA_ERR_UNSUPPORTED,
-              "num_pages*128*num_heads must fit in int32 (virtual page ids)");
   const int64_t rows64 = (int64_t)batch->num_queries * Hkv;
   MSA_REQUIRE(rows64 * k <= 0x7fffffffLL, MSA_ERR_UNSUPPORTED, "num_queries*num_heads*k must fit in int32");
   if (batch->num_queries == 0) return MSA_OK;
@@ -376,13 +399,13 @@ msa_status topk_attn_decode(const msa_batch* batch, const float* scores, int32_t
   if (batch->max_blocks <= msa::select_attend_max_blocks())
     return from_hip(msa::launch_select_attend(batch->num_requests, batch->num_queries, Hkv, batch->max_blocks,
                                               batch->block_table, batch->ctx_len, batch->cu_q, batch->q_pos, scores,
-                                              k, sel, cnt, page_table, row_len, G, D, q, k_cache.data, v_cache.data,
-                                              sm_scale, out, lse, ws.o, ws.lse, ws.counters, st),
+                                              k, sel, cnt, page_table, row_len, vps, G, D, q, k_cache.data,
+                                              v_cache.data, sm_scale, out, lse, ws.o, ws.lse, ws.counters, st),
                     "msa_topk_attn_decode launch");
   // rows too long to select inside the attention workgroup: the two launches of the separate calls
   hipError_t e = msa::launch_topk_page_table(batch->num_requests, batch->num_queries, Hkv, batch->max_blocks,
                                              batch->block_table, batch->ctx_len, batch->cu_q, batch->q_pos, scores, k,
-                                             sel, cnt, page_table, row_len, st);
+                                             sel, cnt, vps, page_table, row_len, st);
   if (e != hipSuccess) return from_hip(e, "msa_topk_attn_decode top-k launch");
   return from_hip(msa::launch_attn_decode(rows, G, D, q, k_cache.data, v_cache.data, D, (int64_t)Hkv * D, page_table,
                                           k, row_len, sm_scale, out, lse, ws.o, ws.lse, ws.counters, st),
@@ -424,8 +447,8 @@ msa_status msa_sparse_attn_prefill(const msa_batch* batch, int32_t G, const void
   if (msa_status s = check_cache(k_cache, "k_cache")) return s;
   if (msa_status s = check_cache(v_cache, "v_cache")) return s;
   MSA_REQUIRE(k_cache.num_pages == v_cache.num_pages && k_cache.num_heads == v_cache.num_heads &&
-                  k_cache.head_dim == v_cache.head_dim,
-              MSA_ERR_INVALID_ARG, "k_cache and v_cache shapes differ");
+                  k_cache.head_dim == v_cache.head_dim && page_elems(k_cache) == page_elems(v_cache),
+              MSA_ERR_INVALID_ARG, "k_cache and v_cache differ in shape or page stride");
   MSA_REQUIRE(supported_group(G), MSA_ERR_UNSUPPORTED, "G must be 1, 2, 4, 8 or 16, got %d", G);
   MSA_REQUIRE(k >= 1 && k <= kMaxK, MSA_ERR_UNSUPPORTED, "k must be in [1, %d], got %d", kMaxK, k);
   MSA_REQUIRE(tile_min_rows >= 0, MSA_ERR_INVALID_ARG, "tile_min_rows must be >= 0, got %d", tile_min_rows);
@@ -447,8 +470,9 @@ msa_status msa_sparse_attn_prefill(const msa_batch* batch, int32_t G, const void
   return from_hip(msa::launch_attn_prefill(batch->num_requests, batch->num_queries, k_cache.num_heads, G,
                                            k_cache.head_dim, batch->max_blocks, batch->max_q_per_request,
                                            batch->block_table, batch->ctx_len, batch->cu_q, batch->q_pos, q,
-                                           k_cache.data, v_cache.data, sel, cnt, k, sm_scale, tile_min_rows, part_o,
-                                           part_lse, slot_of, workspace, reinterpret_cast<hipStream_t>(stream)),
+                                           k_cache.data, v_cache.data, page_elems(k_cache), sel, cnt, k, sm_scale,
+                                           tile_min_rows, part_o, part_lse, slot_of, workspace,
+                                           reinterpret_cast<hipStream_t>(stream)),
                   "msa_sparse_attn_prefill launch");
 }
 

@@ -51,15 +51,16 @@ class MSADecode:
     def score(self, q_idx, kidx, stream=None):
         msa_index_score(self.batch, q_idx, kidx, self.scores, stream)
 
-    def select(self, stream=None):
-        """Top-k and page table only (the "page_table" and "separate" modes)."""
+    def select(self, kcache, stream=None):
+        """Top-k and page table only (the "page_table" and "separate" modes); the page ids follow the K
+        cache's layout (its page stride)."""
         if self.select_mode == "separate":
             msa_topk_blocks(self.batch, self.Hkv, self.scores, self.k, self.sel, self.cnt, stream)
-            msa_build_sparse_page_table(self.batch, self.Hkv, self.num_pages, self.sel, self.cnt, self.k,
-                                        self.page_table, self.row_len, stream)
+            msa_build_sparse_page_table(self.batch, kcache, self.sel, self.cnt, self.k, self.page_table, self.row_len,
+                                        stream)
         else:
-            msa_topk_page_table(self.batch, self.Hkv, self.num_pages, self.scores, self.k, self.sel, self.cnt,
-                                self.page_table, self.row_len, stream)
+            msa_topk_page_table(self.batch, kcache, self.scores, self.k, self.sel, self.cnt, self.page_table,
+                                self.row_len, stream)
 
     def attend(self, q, kcache, vcache, sm_scale: float, stream=None):
         """Decode attention over the page table written by select()."""
@@ -72,7 +73,7 @@ class MSADecode:
             msa_topk_attn_decode(self.batch, self.scores, self.k, kcache, vcache, self.G, q, sm_scale, self.sel,
                                  self.cnt, self.page_table, self.row_len, self.out, self.lse, self.ws, stream)
         else:
-            self.select(stream)
+            self.select(kcache, stream)
             self.attend(q, kcache, vcache, sm_scale, stream)
 
     def __call__(self, q, q_idx, kcache, vcache, kidx, sm_scale: float, stream=None):
@@ -172,9 +173,9 @@ class MSAPrefillQueryMajor:
     def score(self, q_idx, kidx, stream=None):
         msa_index_score(self.batch, q_idx, kidx, self.scores, stream)
 
-    def select(self, stream=None):
-        msa_topk_page_table(self.batch, self.Hkv, self.num_pages, self.scores, self.k, self.sel, self.cnt,
-                            self.page_table, self.row_len, stream)
+    def select(self, kcache, stream=None):
+        msa_topk_page_table(self.batch, kcache, self.scores, self.k, self.sel, self.cnt, self.page_table,
+                            self.row_len, stream)
 
     def attend(self, q, kcache, vcache, sm_scale: float, stream=None):
         msa_sparse_attn_decode(self.rows, self.G, self.D, q, kcache, vcache, self.D, self.Hkv * self.D,
@@ -182,6 +183,6 @@ class MSAPrefillQueryMajor:
 
     def __call__(self, q, q_idx, kcache, vcache, kidx, sm_scale: float, stream=None):
         self.score(q_idx, kidx, stream)
-        self.select(stream)
+        self.select(kcache, stream)
         self.attend(q, kcache, vcache, sm_scale, stream)
         return self.out, self.lse

@@ -65,13 +65,21 @@ typedef struct msa_batch {
   const int32_t* q_pos;        /* device [Nq]: absolute position of each query row */
 } msa_batch;
 
-/* A paged cache: device bf16 [num_pages, block_size, num_heads, head_dim], contiguous. */
+/* A paged cache: device bf16 pages of [block_size, num_heads, head_dim] elements (token rows of
+ * num_heads*head_dim contiguous elements), page p starting at data + p*page_stride elements.
+ * page_stride = 0 means block_size*num_heads*head_dim (pages back to back: [num_pages, block_size,
+ * num_heads, head_dim] contiguous).  A larger stride takes pages spaced apart, e.g. the K and V halves
+ * of a pool laid out [num_pages, 2, block_size, num_heads, head_dim] (both with page_stride =
+ * 2*block_size*num_heads*head_dim).  A nonzero page_stride must be at least block_size*num_heads*
+ * head_dim and a multiple of 8 (16-byte aligned pages); a K or V cache's must also be a multiple of
+ * head_dim (virtual page ids below).  Pages must not overlap. */
 typedef struct msa_cache {
   const void* data;
   int32_t num_pages;
   int32_t block_size;          /* 128 */
   int32_t num_heads;           /* Hkv */
   int32_t head_dim;            /* D (keys/values) or Di (key index) */
+  int64_t page_stride;         /* elements from one page to the next; 0 = block_size*num_heads*head_dim */
 } msa_cache;
 
 /* Stage 1, index scoring (Chinese page, section "索引评分器成为解码关键路径"; Japanese page,
@@ -114,24 +122,26 @@ size_t msa_index_topk_workspace_size(const msa_batch* batch, int32_t num_kv_head
 
 /* Sparse per-row page table for decode (Chinese page, section "MSA需要新的分页注意力集成"):
  * row rho = t*Hkv + g of the flattened (query row, KV head) batch gets
- *   page_table[rho, j] = block_table[r, sel[t,g,j]] * 128 * Hkv + g   (j < cnt[t,g]; -1 after)
- * a virtual page id in the strided view of a [pages, 128, Hkv, D] cache whose page
+ *   page_table[rho, j] = block_table[r, sel[t,g,j]] * (P / D) + g   (j < cnt[t,g]; -1 after)
+ * with P the cache's page stride in elements (128 * Hkv * D for back-to-back pages, which gives the
+ * pages' block_table * 128 * Hkv + g): a virtual page id in the strided view of the cache whose page
  * stride is D elements and token stride Hkv*D elements, and
  *   row_len[rho] = number of valid tokens over the selected blocks (only the last,
  *                  highest block can be partial).
- * num_pages is the page count of the cache; num_pages*128*Hkv must fit in int32.
+ * kv_layout describes the K (or V: the same layout) cache; only its shape and page stride are read
+ * (data may be NULL).  Hkv = kv_layout.num_heads; num_pages * P / D must fit in int32.
  *   page_table  device i32 [Nq*Hkv, k];  row_len  device i32 [Nq*Hkv] */
-msa_status msa_build_sparse_page_table(const msa_batch* batch, int32_t num_kv_heads, int32_t num_pages,
-                                       const int32_t* sel, const int32_t* cnt, int32_t k,
-                                       int32_t* page_table, int32_t* row_len, msa_stream_t stream);
+msa_status msa_build_sparse_page_table(const msa_batch* batch, msa_cache kv_layout, const int32_t* sel,
+                                       const int32_t* cnt, int32_t k, int32_t* page_table, int32_t* row_len,
+                                       msa_stream_t stream);
 
 /* msa_topk_blocks followed by msa_build_sparse_page_table, in one launch when the rows fit the
  * register top-k (max_blocks <= 16384), else in two.
  * Same arguments, outputs and results as the two calls; the fusion is the one the pages name as
  * open for MSA's small kernels (Chinese page, section "遗留问题"). */
-msa_status msa_topk_page_table(const msa_batch* batch, int32_t num_kv_heads, int32_t num_pages,
-                               const float* scores, int32_t k, int32_t* sel, int32_t* cnt, int32_t* page_table,
-                               int32_t* row_len, msa_stream_t stream);
+msa_status msa_topk_page_table(const msa_batch* batch, msa_cache kv_layout, const float* scores, int32_t k,
+                               int32_t* sel, int32_t* cnt, int32_t* page_table, int32_t* row_len,
+                               msa_stream_t stream);
 
 /* Decode attention over the sparse page table (same section): each row rho attends with its
  * G query heads q[rho*G .. rho*G+G-1] to the first row_len[rho] tokens of its virtual pages.

@@ -68,7 +68,7 @@ def page_table(dev, b, sel, cnt, k=None):
     k = k or wl.k
     pt = poison_i32(wl.Nq * wl.Hkv, k)
     rl = poison_i32(wl.Nq * wl.Hkv)
-    lib().msa_build_sparse_page_table(b, wl.Hkv, dev.kcache.shape[0], sel, cnt, k, pt, rl)
+    lib().msa_build_sparse_page_table(b, dev.kcache, sel, cnt, k, pt, rl)
     return pt, rl
 
 
@@ -78,7 +78,7 @@ def topk_page_table(dev, b, s, k=None):
     k = k or wl.k
     sel, cnt = poison_i32(wl.Nq, wl.Hkv, k), poison_i32(wl.Nq, wl.Hkv)
     pt, rl = poison_i32(wl.Nq * wl.Hkv, k), poison_i32(wl.Nq * wl.Hkv)
-    lib().msa_topk_page_table(b, wl.Hkv, dev.kcache.shape[0], s, k, sel, cnt, pt, rl)
+    lib().msa_topk_page_table(b, dev.kcache, s, k, sel, cnt, pt, rl)
     return sel, cnt, pt, rl
 
 

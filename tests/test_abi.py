@@ -55,8 +55,8 @@ def _batch(B=2, Nq=2, max_blocks=4, maxq=1, **over):
     return _lib.MsaBatch(**kw)
 
 
-def _cache(P=8, BS=128, H=2, D=64, data=FAKE):
-    return _lib.MsaCache(data, P, BS, H, D)
+def _cache(P=8, BS=128, H=2, D=64, data=FAKE, page_stride=0):
+    return _lib.MsaCache(data, P, BS, H, D, page_stride)
 
 
 @no_gpu
@@ -92,22 +92,44 @@ def test_topk_rejects(lib, k, hkv, status):
 @no_gpu
 def test_page_table_rejects_overflowing_virtual_ids(lib):
     b = _batch()
-    assert lib.msa_build_sparse_page_table(ctypes.byref(b), 8, 1 << 22, FAKE, FAKE, 16, FAKE, FAKE, None) == UNSUPPORTED
+    kv = _cache(P=1 << 22, H=8)
+    assert lib.msa_build_sparse_page_table(ctypes.byref(b), kv, FAKE, FAKE, 16, FAKE, FAKE, None) == UNSUPPORTED
+    # a page stride of twice the page (K and V pages interleaved) doubles the virtual ids
+    kv = _cache(P=1 << 20, H=8, page_stride=2 * 128 * 8 * 64)
+    assert lib.msa_build_sparse_page_table(ctypes.byref(b), kv, FAKE, FAKE, 16, FAKE, FAKE, None) == UNSUPPORTED
+    kv = _cache(P=1 << 19, H=8, page_stride=2 * 128 * 8 * 64)  # fits: the call gets past its checks
+    assert lib.msa_build_sparse_page_table(ctypes.byref(_batch(Nq=0)), kv, FAKE, FAKE, 16, FAKE, FAKE, None) == OK
 
 
 @no_gpu
-@pytest.mark.parametrize("hkv,pages,k,status", [(2, 8, 0, UNSUPPORTED), (2, 8, 65, UNSUPPORTED),
-                                                (0, 8, 4, UNSUPPORTED), (2, 0, 4, INVALID),
-                                                (8, 1 << 22, 16, UNSUPPORTED)])
-def test_topk_page_table_rejects(lib, hkv, pages, k, status):
+@pytest.mark.parametrize("hkv,pages,k,ps,status", [(2, 8, 0, 0, UNSUPPORTED), (2, 8, 65, 0, UNSUPPORTED),
+                                                   (0, 8, 4, 0, UNSUPPORTED), (2, 0, 4, 0, INVALID),
+                                                   (8, 1 << 22, 16, 0, UNSUPPORTED),
+                                                   # page strides: below the page, unaligned, not whole in D
+                                                   (2, 8, 4, 128 * 2 * 64 - 8, INVALID), (2, 8, 4, 128 * 2 * 64 + 4, INVALID),
+                                                   (2, 8, 4, 128 * 2 * 64 + 8, INVALID)])
+def test_topk_page_table_rejects(lib, hkv, pages, k, ps, status):
     b = _batch()
-    assert lib.msa_topk_page_table(ctypes.byref(b), hkv, pages, FAKE, k, FAKE, FAKE, FAKE, FAKE, None) == status
+    kv = _cache(P=pages, H=hkv, page_stride=ps)
+    assert lib.msa_topk_page_table(ctypes.byref(b), kv, FAKE, k, FAKE, FAKE, FAKE, FAKE, None) == status
 
 
 @no_gpu
 def test_topk_page_table_rejects_null_outputs(lib):
     b = _batch()
-    assert lib.msa_topk_page_table(ctypes.byref(b), 2, 8, FAKE, 4, FAKE, FAKE, None, FAKE, None) == INVALID
+    assert lib.msa_topk_page_table(ctypes.byref(b), _cache(), FAKE, 4, FAKE, FAKE, None, FAKE, None) == INVALID
+
+
+@no_gpu
+def test_cache_page_stride_checks(lib):
+    """A cache's page stride: 0 or at least one page, 16-byte aligned; K and V alike."""
+    b = _batch()
+    page = 128 * 2 * 64
+    assert lib.msa_index_score(ctypes.byref(b), FAKE, _cache(page_stride=page - 64), FAKE, None) == INVALID
+    assert lib.msa_index_score(ctypes.byref(b), FAKE, _cache(page_stride=page + 4), FAKE, None) == INVALID
+    args = (FAKE, 4, _cache(page_stride=2 * page), _cache(page_stride=page), 8, FAKE, 0.1, FAKE, FAKE, FAKE, FAKE,
+            FAKE, FAKE, FAKE, 1 << 30, None)
+    assert lib.msa_topk_attn_decode(ctypes.byref(b), *args) == INVALID  # K and V page strides differ
 
 
 @no_gpu
@@ -190,7 +212,7 @@ def test_empty_inputs_launch_nothing(lib):
     b = _batch(Nq=0)
     assert lib.msa_index_score(ctypes.byref(b), None, _cache(), None, None) == OK
     assert lib.msa_topk_blocks(ctypes.byref(b), 2, None, 4, None, None, None) == OK
-    assert lib.msa_topk_page_table(ctypes.byref(b), 2, 8, None, 4, None, None, None, None, None) == OK
+    assert lib.msa_topk_page_table(ctypes.byref(b), _cache(), None, 4, None, None, None, None, None) == OK
     assert lib.msa_topk_attn_decode(ctypes.byref(b), None, 4, _cache(), _cache(), 8, None, 0.1, None, None, None,
                                     None, None, None, None, 0, None) == OK
     assert lib.msa_lse_merge(0, 4, 8, 128, None, None, None, None, None) == OK

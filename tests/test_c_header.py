@@ -24,9 +24,9 @@ int main(void) {
          offsetof(msa_batch, num_queries), offsetof(msa_batch, max_blocks), offsetof(msa_batch, max_q_per_request),
          offsetof(msa_batch, block_table), offsetof(msa_batch, ctx_len), offsetof(msa_batch, cu_q),
          offsetof(msa_batch, q_pos));
-  printf("cache %zu %zu %zu %zu %zu %zu\n", sizeof(msa_cache), offsetof(msa_cache, data),
+  printf("cache %zu %zu %zu %zu %zu %zu %zu\n", sizeof(msa_cache), offsetof(msa_cache, data),
          offsetof(msa_cache, num_pages), offsetof(msa_cache, block_size), offsetof(msa_cache, num_heads),
-         offsetof(msa_cache, head_dim));
+         offsetof(msa_cache, head_dim), offsetof(msa_cache, page_stride));
   printf("version %d\n", msa_version());
   printf("status %s\n", msa_status_string(MSA_ERR_WORKSPACE_TOO_SMALL));
   /* rejected on the host before any launch: no device is touched */
