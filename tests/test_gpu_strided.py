@@ -89,6 +89,15 @@ def test_decode_on_strided_caches(name):
     out, lse = decode_attention(sd, pt, rl)
     out_c, lse_c = decode_attention(dev, ref[2], ref[3])
     assert _same(out, out_c) and _same(lse, lse_c)
+    # the allocation-free entry point on the same views
+    rows = wl.Nq * wl.Hkv
+    bufs = (poison_i32(wl.Nq, wl.Hkv, wl.k), poison_i32(wl.Nq, wl.Hkv), poison_i32(rows, wl.k), poison_i32(rows),
+            torch.full((wl.Nq, wl.Hq, wl.D), float("nan"), dtype=torch.bfloat16, device="cuda"),
+            torch.full((wl.Nq, wl.Hq), float("nan"), dtype=torch.float32, device="cuda"))
+    lib().msa_topk_attn_decode_noalloc(b, s, wl.k, sd.kcache, sd.vcache, wl.G, dev.q, dev.scale, *bufs)
+    torch.cuda.synchronize()
+    for x, y in zip(bufs, got):
+        assert _same(x, y), "allocation-free route differs on the strided caches"
 
 
 @pytest.mark.parametrize("name", list(PREFILL))
