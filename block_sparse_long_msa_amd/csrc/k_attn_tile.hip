@@ -284,8 +284,13 @@ __global__ __launch_bounds__(kTileThreads, 1) void k_attn_tile(
   __shared__ uint16_t s_union[kDenseMax]; // the bucket's dense blocks, ascending
   __shared__ int s_ncov[TT], s_t[TT], s_jt[TT], s_pos[TT];
 
-  const int item = blockIdx.x;            // consecutive tiles on consecutive XCDs: one KV head at a time
-  if (item >= tile_count[0]) return;
+  // XCD-aware: the workgroups of one XCD take one contiguous run of tiles, so a bucket's tiles share
+  // that XCD's L2 for the bucket's dense blocks
+  const int ntile = tile_count[0];
+  const int per_xcd = (ntile + 7) / 8;
+  const int slot = (int)blockIdx.x / 8;
+  const int item = ((int)blockIdx.x % 8) * per_xcd + slot;
+  if (slot >= per_xcd || item >= ntile) return;
   const int2 tl = tiles[item];
   const int64_t bucket = tl.x;
   const int nu = dense_n[bucket];
@@ -648,7 +653,7 @@ hipError_t launch_attn_tiles(int64_t max_tiles, int B, int Hkv, int G, int D, in
                              const int32_t* dense_n, const uint64_t* cov_mask, const int32_t* row_jt,
                              const int2* tiles, const int32_t* tile_count, float scale_log2, void* part_o,
                              float* part_lse, hipStream_t stream) {
-  const unsigned grid = (unsigned)max_tiles;
+  const unsigned grid = (unsigned)((max_tiles + 7) / 8 * 8);
   if (grid == 0) return hipSuccess;
   const bf16* qq = static_cast<const bf16*>(q);
   const bf16* kc = static_cast<const bf16*>(kcache);

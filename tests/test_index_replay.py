@@ -159,6 +159,20 @@ def replay_tiles(x, Hkv, G, D, k, n_min):
             groups.setdefault((g * B + seg0, order[0], order[1] if len(order) > 1 else -1), []).append(t)
     TT = 256 // G
     tpw = 16 * TILE_NT // G
+    # the launch: grid = a bound on the tiles rounded up to whole XCD rounds; workgroup -> tile as in the
+    # kernel (each XCD takes one contiguous run of tiles), every tile exactly once
+    n_tiles = sum(-(-len(rows) // TT) for rows in groups.values())
+    for bound in (n_tiles, n_tiles + 5, 2 * n_tiles + 13):
+        grid = -(-bound // K_XCDS) * K_XCDS
+        per_xcd = -(-n_tiles // K_XCDS)
+        seen = np.zeros(n_tiles, dtype=int)
+        for wg in range(grid):
+            slot = wg // K_XCDS
+            item = (wg % K_XCDS) * per_xcd + slot
+            if slot >= per_xcd or item >= n_tiles:
+                continue
+            seen[item] += 1
+        assert np.all(seen == 1), "every tile runs exactly once"
     covered = np.zeros(sel.shape, dtype=bool)
     for (seg, _, _), rows in groups.items():
         g, r = seg // B, seg % B
