@@ -158,7 +158,9 @@ __global__ __launch_bounds__(64 * NW) void k_topk(int B, int Hkv, int max_blocks
 // The same selection for rows whose candidates fit in registers (64*NW*R >= n): every lane
 // reads its R scores once and row_topk (topk_select.h) finds the k-th largest key bit by bit with
 // ballot counts.  Against the radix passes it saves the re-reads of the scores and the LDS
-// histogram round trips.
+// histogram round trips.  With TL (the longest register rows) the selection is two-level
+// (row_topk_two_level): each wave takes the top k of its own run of ids without a workgroup barrier
+// per trial bit, and wave 0 the top k of those candidates.
 //
 // With page_table != NULL the same launch also writes the row's decode page table and row length
 // (as k_page_table below), from the chosen ids kept in LDS; the request lookup is issued at the
@@ -173,13 +175,13 @@ struct PageTableOut {
   int vps;              // virtual pages per physical page: the cache's page stride / D
 };
 
-template <int NW, int R>
+template <int NW, int R, bool TL>
 __global__ __launch_bounds__(64 * NW) void k_topk_reg(int Hkv, int max_blocks, const int32_t* __restrict__ q_pos,
                                                       const float* __restrict__ scores, int k,
                                                       int32_t* __restrict__ sel, int32_t* __restrict__ cnt,
                                                       PageTableOut pto) {
   constexpr int NT = 64 * NW;
-  __shared__ RowTopkLds<NW> sh;
+  __shared__ std::conditional_t<TL, RowTopk2Lds<NW>, RowTopkLds<NW>> sh;
   __shared__ int s_sel[64];
   const int row = blockIdx.x;  // t*Hkv + g
   const int t = row / Hkv;
@@ -188,11 +190,12 @@ __global__ __launch_bounds__(64 * NW) void k_topk_reg(int Hkv, int max_blocks, c
   const int n = min(pos / kBlock + 1, max_blocks);
   const float* s = scores + (int64_t)row * max_blocks;
   int32_t* out = sel + (int64_t)row * k;
-  // id i = tid + NT*r.  All R loads are unconditional (clamped to the row's max_blocks entries)
-  // and go out together with the row's position and the request lookup for the page table.
+  // id i = tid + NT*r (TL: wv*64*R + lane + 64*r).  All R loads are unconditional (clamped to the
+  // row's max_blocks entries) and go out together with the row's position and the request lookup
+  // for the page table.
   float v[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) v[r] = s[min(tid + NT * r, max_blocks - 1)];
+  for (int r = 0; r < R; ++r) v[r] = s[min(TL ? wv * 64 * R + lane + 64 * r : tid + NT * r, max_blocks - 1)];
   int r_req = 0, lim = 0;
   if (pto.page_table) {
     int L;
@@ -202,10 +205,13 @@ __global__ __launch_bounds__(64 * NW) void k_topk_reg(int Hkv, int max_blocks, c
 #pragma unroll
   for (int r = 0; r < R; ++r) asm volatile("" ::"v"(v[r]));
 
-  const int c = row_topk<NW, R>(v, n, k, sh, [&](int slot, int id, int) {
+  auto keep = [&](int slot, int id) {
     out[slot] = id;
     s_sel[slot] = id;
-  });
+  };
+  int c;
+  if constexpr (TL) c = row_topk_two_level<NW, R>(v, n, k, sh, keep);
+  else c = row_topk<NW, R>(v, n, k, sh, [&](int slot, int id, int) { keep(slot, id); });
   for (int i = c + tid; i < k; i += NT) out[i] = -1;
   if (tid == 0) cnt[row] = c;
   if (pto.page_table) {  // the chosen ids, in ascending order, are in s_sel[0 .. c-1]
@@ -257,11 +263,16 @@ __global__ __launch_bounds__(256) void k_page_table(int rows, int B, int Hkv, in
   if (j == 0) row_len[rho] = len;
 }
 
+// Rows of 8193 to 16384 blocks (16 waves, 16 scores per lane) select in two levels: top-k plus page
+// table 30.6 -> 20.5 us on two 11,719-block rows (events, bit-identical).  With 8 scores per lane the
+// one-level search is as fast or faster (8192 blocks: 14.7 / 14.9 us against 14.4 / 15.6 us at one and
+// four requests; 4 waves x 8: 11.6 against 12.6 us), so those layouts keep it.
 template <int NW, int R>
 static void launch_reg(int rows, hipStream_t stream, int Hkv, int max_blocks, const int32_t* q_pos,
                        const float* scores, int k, int32_t* sel, int32_t* cnt, const PageTableOut& pto) {
-  hipLaunchKernelGGL((k_topk_reg<NW, R>), dim3(rows), dim3(64 * NW), 0, stream, Hkv, max_blocks, q_pos, scores, k,
-                     sel, cnt, pto);
+  constexpr bool TL = NW == 16 && R == 16;
+  hipLaunchKernelGGL((k_topk_reg<NW, R, TL>), dim3(rows), dim3(64 * NW), 0, stream, Hkv, max_blocks, q_pos, scores,
+                     k, sel, cnt, pto);
 }
 
 // Top-k, and with pto.page_table set also the decode page table.  Returns false (nothing

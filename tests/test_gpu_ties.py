@@ -9,7 +9,9 @@ Half the rows get the copy at a lower block id (which must then replace the k-th
 higher one (which must stay out).  The selections of msa_topk_blocks, msa_topk_page_table and
 msa_topk_attn_decode must then equal the oracle's top-k on the oracle's own fp64 scores, with no
 boundary excusal.  Context lengths walk through the register layouts of the top-k (one wave with
-1, 4 and 8 scores per lane, 4 waves, 16 waves) and the radix select beyond 16,384 blocks.
+1, 4 and 8 scores per lane; 4 and 16 waves with 8 and 16 scores per lane, which select in two levels,
+so a copy often lands in another wave's run of ids than the block it ties) and the radix select beyond
+16,384 blocks.
 """
 import numpy as np
 import pytest
@@ -26,10 +28,12 @@ CASES = {  # name: (context lengths, Hkv, k)
     "one_wave_4_per_lane": ([30000, 25000], 2, 16),
     "one_wave_8_per_lane": ([60000, 50001], 2, 16),
     "four_waves": ([140000, 190000], 2, 33),
+    "four_waves_16_per_lane": ([300000, 400000], 2, 24),
     "sixteen_waves": ([524300], 1, 32),
+    "sixteen_waves_16_per_lane": ([1500000], 1, 48),
     "radix_select": ([2100000], 1, 9),
 }
-GPU_DRAWN = {"sixteen_waves", "radix_select"}
+GPU_DRAWN = {"sixteen_waves", "sixteen_waves_16_per_lane", "radix_select"}
 
 
 def _order(row, n):
