@@ -32,6 +32,9 @@ CASES = {
     "topk_16_waves": dict(ctx=[524300, 300001], nq=[1, 1], Hq=4, Hkv=1, D=64, Di=64, k=20),
     # 16 waves with 16 scores per lane (8193 to 16384 blocks): the two-level selection
     "topk_16_waves_two_level": dict(ctx=[1500000, 1100000], nq=[1, 1], Hq=4, Hkv=1, D=64, Di=64, k=40),
+    # its edges: 8193 blocks (the last wave holds one candidate) and the largest k; a wave run of ids
+    # ends exactly at the second row's last block
+    "topk_two_level_edges": dict(ctx=[1048577, 1179648], nq=[1, 1], Hq=4, Hkv=1, D=64, Di=64, k=64),
     "topk_4_waves": dict(ctx=[190000, 140000], nq=[1, 1], Hq=8, Hkv=2, D=64, Di=64, k=33),
     # one wave holding 4 and 8 scores per lane (up to 256 / 512 blocks)
     "topk_4_per_lane": dict(ctx=[30000, 700], nq=[1, 2], Hq=8, Hkv=2, D=64, Di=64, k=7),
@@ -46,7 +49,7 @@ CASES = {
     # the most KV heads the library takes (64, one query head each) with the largest k
     "hkv64_g1_k64": dict(ctx=[9000, 700], nq=[1, 2], Hq=64, Hkv=64, D=64, Di=64, k=64),
 }
-GPU_DRAWN = {"topk_16_waves", "topk_16_waves_two_level", "topk_radix_long_rows"}   # inputs drawn on the GPU, copied to the host
+GPU_DRAWN = {"topk_16_waves", "topk_16_waves_two_level", "topk_two_level_edges", "topk_radix_long_rows"}   # inputs drawn on the GPU, copied to the host
 
 
 def _wl(name, seed=21):
