@@ -8,11 +8,11 @@
 // k_attn_decode: one workgroup per (row, run of pages); the four waves take 32 tokens of every
 //   page each and keep a running softmax over the run.
 //   S^T = K Q^T on bf16 MFMA with the tokens as M and the G query heads padded into N.
-//   P stays in the MFMA result registers and feeds O^T = V^T P^T directly as the B operand of
-//   an fp32 16x16x4 MFMA: lane (n, q) holds P for tokens 4q+i, and loads the matching V row
-//   as 16 contiguous bytes, whose 8 values become the A operand of 8 MFMAs (output row m of
-//   MFMA c is d = 8m + c).  No LDS transpose, no shuffles, every V row read as whole
-//   64-byte segments.  The four waves' (max, sum, O) are combined through LDS.  A row is split
+//   P stays in the registers of the MFMA result that produced it and feeds O^T = V^T P^T as the
+//   (bf16) B operand of a 16x16x32 MFMA: lane (n, q) holds P for its 8 tokens, and loads the same
+//   tokens' V rows as 16 contiguous bytes each, whose element c over the 8 tokens becomes the A
+//   operand of MFMA c (output row m of MFMA c is d = 8m + c).  No LDS transpose, no shuffles, every
+//   V row read as whole 64-byte segments.  The four waves' (max, sum, O) are combined through LDS.  A row is split
 //   over several workgroups only as far as needed to occupy the chip; the last split of a row to
 //   finish combines the row's split partials (merge_row), so there is no second launch, or, for
 //   rows split more than kFusedMergeMax ways, k_merge_splits does.
@@ -110,18 +110,29 @@ __device__ __forceinline__ void attend_page(const PageRegs<D>& r, const u32x4 (&
   for (int c = 0; c < 8; ++c)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[c][e] *= alpha;
+  // O^T += V^T P^T on bf16 MFMA over the wave's 32 tokens, in the order the S tiles hold them: k slot
+  // 8qd + j of lane group qd is token 4qd + j (j < 4) or 16 + 4qd + j - 4.  B = P^T: lane (n, qd)
+  // already holds its 8 tokens' probabilities for head n.  A for MFMA c = V^T rows d = 8m + c: lane
+  // (m, qd) loaded 8 consecutive d of each of the same 8 tokens, so its A operand is element c of those
+  // 8 loads, regrouped in registers.
+  u32x4 pb;
+  pb[0] = pack_bf2(s[0][0], s[0][1]);
+  pb[1] = pack_bf2(s[0][2], s[0][3]);
+  pb[2] = pack_bf2(s[1][0], s[1][1]);
+  pb[3] = pack_bf2(s[1][2], s[1][3]);
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 v = r.v[sub][i];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint32_t word = v[c >> 1];
-        const float vf = (c & 1) ? __uint_as_float(word & 0xffff0000u) : __uint_as_float(word << 16);
-        acc[c] = mfma_f32(vf, s[sub][i], acc[c]);
-      }
-    }
+  for (int c = 0; c < 8; ++c) {
+    const int e = c >> 1;
+    auto pair = [&](const u32x4& x, const u32x4& y) {  // element c of x (low half), of y (high half)
+      return (c & 1) ? ((x[e] >> 16) | (y[e] & 0xffff0000u)) : ((x[e] & 0xffffu) | (y[e] << 16));
+    };
+    u32x4 a;
+    a[0] = pair(r.v[0][0], r.v[0][1]);
+    a[1] = pair(r.v[0][2], r.v[0][3]);
+    a[2] = pair(r.v[1][0], r.v[1][1]);
+    a[3] = pair(r.v[1][2], r.v[1][3]);
+    acc[c] = mfma_bf16(a, pb, acc[c]);
+  }
 }
 
 // LDS of one decode attention workgroup: the four waves' (max, sum, O) for the final combine.
