@@ -11,8 +11,9 @@
 //   P stays in the registers of the MFMA result that produced it and feeds O^T = V^T P^T as the
 //   (bf16) B operand of a 16x16x32 MFMA: lane (n, q) holds P for its 8 tokens, and loads the same
 //   tokens' V rows as 16 contiguous bytes each, whose element c over the 8 tokens becomes the A
-//   operand of MFMA c (output row m of MFMA c is d = 8m + c).  No LDS transpose, no shuffles, every
-//   V row read as whole 64-byte segments.  The four waves' (max, sum, O) are combined through LDS.  A row is split
+//   operand of MFMA c (output row m of MFMA c is d = 8m + c).  No LDS transpose, no shuffles,
+//   every V row read as whole 64-byte segments.  The four waves' (max, sum, O) are combined
+//   through LDS.  A row is split
 //   over several workgroups only as far as needed to occupy the chip; the last split of a row to
 //   finish combines the row's split partials (merge_row), so there is no second launch, or, for
 //   rows split more than kFusedMergeMax ways, k_merge_splits does.
