@@ -13,10 +13,9 @@
 //   tokens' V rows as 16 contiguous bytes each, whose element c over the 8 tokens becomes the A
 //   operand of MFMA c (output row m of MFMA c is d = 8m + c).  No LDS transpose, no shuffles,
 //   every V row read as whole 64-byte segments.  The four waves' (max, sum, O) are combined
-//   through LDS.  A row is split
-//   over several workgroups only as far as needed to occupy the chip; the last split of a row to
-//   finish combines the row's split partials (merge_row), so there is no second launch, or, for
-//   rows split more than kFusedMergeMax ways, k_merge_splits does.
+//   through LDS.  A row is split over several workgroups only as far as needed to occupy the chip;
+//   the last split of a row to finish combines the row's split partials (merge_row), so there is
+//   no second launch, or, for rows split more than kFusedMergeMax ways, k_merge_splits does.
 // k_select_attend: the top-k, the page table and k_attn_decode in one launch -- each attention
 //   workgroup selects its own row's blocks from the scores (row_topk, topk_select.h) and takes the
 //   chosen pages' ids from LDS instead of a page table in memory.
